@@ -1,0 +1,359 @@
+"""Seeded synthetic workloads for the tiered sparse-MLA decode step.
+
+This module only *generates inputs*: it holds none of the method's
+arithmetic (no top-K, no residency classification, no LRU, no attention).
+Both the CPU oracle (through the tests) and the HIP path (through the
+binding, the tests and the benchmark) consume the exact bytes it produces.
+
+Shapes follow the pages' description of the method:
+  * latent MLA rows of 512 "nope" + 64 "rope" dims, one per token
+    (page 3, "The core idea of sparse MLA" and the MLA note below it);
+  * a paged KV pool with 64-token pages (page 3, the PagedAttention note);
+  * a per-request GPU/host residency per page (page 2, "Technical
+    implementation of Hybrid HiSparse", the three residency states);
+  * a per-request hot buffer of 2x top-K rows leased from the pool
+    (page 2, "Key architecture details", first bullet);
+  * the agent workload shape: 74,160-token first turn, 753-token later
+    turns, 220 output tokens, MTP with 3 drafts (page 2, "Performance
+    benchmarking").
+
+Recipe (all draws seeded; every array is produced once on the host):
+  * master seed = 20261202 + c for workload c in 1..5;
+    ``numpy.random.SeedSequence(seed).spawn(6)`` gives independent streams
+    for scores, rows, queries, page placement, context lengths and topic
+    shifts;
+  * latent row t: x = sigma_t * z, z ~ N(0,1)^576, sigma_t = exp(0.5*N(0,1))
+    (per-row log-normal magnitude so per-row fp8 scales differ); stored as
+    fp32, bf16 (round-to-nearest-even) or OCP fp8 e4m3fn codes with one fp32
+    scale per row (scale = amax/448, values clamped to +-448, RNE);
+  * queries N(0,1), fresh every step, fp32 or bf16;
+  * indexer scores fp32: i.i.d. N(0,1), or a per-token AR(1) chain
+    s <- rho*s + eps (eps ~ N(0,1)) whose first value is drawn from the
+    stationary law N(0, 1/(1-rho^2)); the 1M workload redraws every chain
+    from the stationary law on 5% of steps (topic shift);
+  * GPU pages sit at pool page ids taken from a seeded permutation, so the
+    row gathers are scattered; each request leases hot_rows/page_size pool
+    pages for its hot buffer from the same permutation.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+NOPE_DIM = 512
+ROPE_DIM = 64
+ROW_DIM = NOPE_DIM + ROPE_DIM
+PAGE_SIZE = 64
+FP8_MAX = 448.0
+MASTER_SEED = 20261202
+ROW_CHUNK = 65536  # rows generated per draw call (part of the recipe)
+
+KV_F32, KV_BF16, KV_FP8 = "f32", "bf16", "fp8"
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    """One synthetic workload: shapes, dtypes, residency and score process."""
+
+    name: str
+    index: int              # 1..5, selects the master seed
+    n_req: int
+    kv_dtype: str           # f32 | bf16 | fp8
+    q_dtype: str            # f32 | bf16
+    heads: int
+    q_per_req: int
+    top_k: int
+    hot_rows: int
+    steps: int
+    residency: str          # see _gpu_page_mask
+    scores: Tuple           # ("iid",) | ("ar1", rho) | ("ar1_shift", rho, p)
+    ctx: Optional[int] = None          # fixed context length, or None
+    ctx_range: Optional[Tuple[int, int]] = None  # uniform integer range
+    host_pages: Optional[int] = None   # oldest pages on host (fixed-ctx specs)
+    growth: Optional[Tuple[int, int, int, int]] = None  # first, later, out, turns
+    gpu_token_budget: Optional[int] = None  # newest tokens on GPU per request
+    page_size: int = PAGE_SIZE
+
+    @property
+    def seed(self) -> int:
+        return MASTER_SEED + self.index
+
+
+# The five workloads. Sizes in tokens use 1K = 1024.
+SPECS: Dict[str, WorkloadSpec] = {
+    "tiny": WorkloadSpec(
+        name="tiny", index=1, n_req=1, ctx=4096, kv_dtype=KV_F32, q_dtype="f32",
+        heads=16, q_per_req=1, top_k=256, hot_rows=512, steps=8,
+        residency="oldest_host", host_pages=48, scores=("iid",)),
+    "single-128k": WorkloadSpec(
+        name="single-128k", index=2, n_req=1, ctx=131072, kv_dtype=KV_BF16,
+        q_dtype="bf16", heads=128, q_per_req=1, top_k=2048, hot_rows=4096,
+        steps=64, residency="oldest_host", host_pages=1536,
+        scores=("ar1", 0.9)),
+    "batch32": WorkloadSpec(
+        name="batch32", index=3, n_req=32, ctx_range=(16384, 262144),
+        kv_dtype=KV_BF16, q_dtype="bf16", heads=128, q_per_req=1, top_k=2048,
+        hot_rows=4096, steps=32, residency="mod3", scores=("ar1", 0.9)),
+    "single-1m-fp8": WorkloadSpec(
+        name="single-1m-fp8", index=4, n_req=1, ctx=1048576, kv_dtype=KV_FP8,
+        q_dtype="bf16", heads=128, q_per_req=1, top_k=2048, hot_rows=4096,
+        steps=128, residency="oldest_host", host_pages=14745,
+        scores=("ar1_shift", 0.95, 0.05)),
+    "agent16": WorkloadSpec(
+        name="agent16", index=5, n_req=16, kv_dtype=KV_FP8, q_dtype="bf16",
+        heads=128, q_per_req=4, top_k=2048, hot_rows=4096, steps=715,
+        residency="budget", gpu_token_budget=145408, growth=(74160, 753, 220, 13),
+        scores=("ar1", 0.9)),
+    # Aggregate reading of the 142K admission limit: 9,088 newest tokens
+    # (142 pages) of each of the 16 requests stay on GPU.
+    "agent16-b": WorkloadSpec(
+        name="agent16-b", index=5, n_req=16, kv_dtype=KV_FP8, q_dtype="bf16",
+        heads=128, q_per_req=4, top_k=2048, hot_rows=4096, steps=715,
+        residency="budget", gpu_token_budget=9088, growth=(74160, 753, 220, 13),
+        scores=("ar1", 0.9)),
+}
+
+
+def row_bytes(kv_dtype: str) -> int:
+    """Bytes of one stored row payload (the fp8 scale is stored apart)."""
+    return {KV_F32: 4 * ROW_DIM, KV_BF16: 2 * ROW_DIM, KV_FP8: ROW_DIM}[kv_dtype]
+
+
+# ---------------------------------------------------------------- encodings
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (RNE) and return the raw 16-bit patterns."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def f32_rows_to_fp8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Encode rows as OCP e4m3fn codes with one fp32 scale per row."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0))
+    scale = scale.astype(np.float32)
+    y = np.clip(x / scale[:, None], -FP8_MAX, FP8_MAX).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.copy(), scale
+
+
+# ---------------------------------------------------------------- schedules
+def context_schedule(spec: WorkloadSpec, ctx0: np.ndarray, steps: int) -> np.ndarray:
+    """Context length of every request at decode steps 1..steps, [steps, R].
+
+    Fixed-length workloads keep ctx0. The agent workload grows: turn 1 is
+    the first prompt; each turn emits out/Q steps that commit Q tokens each;
+    turns 2.. add a prompt of `later` tokens before their first step.
+    """
+    R = ctx0.shape[0]
+    if spec.growth is None:
+        return np.broadcast_to(ctx0, (steps, R)).astype(np.int64).copy()
+    first, later, out, turns = spec.growth
+    per_turn = out // spec.q_per_req
+    lens = []
+    cur = first
+    for turn in range(turns):
+        if turn > 0:
+            cur += later
+        for _ in range(per_turn):
+            lens.append(cur)
+            cur += spec.q_per_req
+    lens = np.asarray(lens, dtype=np.int64)
+    if steps > lens.size:
+        raise ValueError(f"{spec.name} defines {lens.size} steps")
+    return np.broadcast_to(lens[:steps, None], (steps, R)).copy()
+
+
+def final_context(spec: WorkloadSpec, ctx0: np.ndarray) -> np.ndarray:
+    """Largest context each request reaches over its full schedule."""
+    if spec.growth is None:
+        return ctx0.copy()
+    first, later, out, turns = spec.growth
+    total = first + (turns - 1) * later + turns * out
+    return np.full_like(ctx0, total)
+
+
+@dataclasses.dataclass
+class Workload:
+    """Generated inputs of one workload (host arrays only)."""
+
+    spec: WorkloadSpec
+    ctx0: np.ndarray            # [R] context at step 1
+    ctx_final: np.ndarray       # [R] largest context over the run
+    host_base: np.ndarray       # [R] int64 first row of request r in the store
+    rows: np.ndarray            # logical store: f32 [N,576] | u16 [N,576] | u8 [N,576]
+    scales: Optional[np.ndarray]  # fp8 only: f32 [N]
+    gpu_page: List[np.ndarray]  # per request: int32 [pages(final)], pool page or -1
+    hot_pages: np.ndarray       # [R, hot_rows/page_size] int32 pool pages
+    num_pool_pages: int
+    sm_scale: np.float32
+    _streams: Dict[str, np.random.Generator] = dataclasses.field(repr=False, default_factory=dict)
+
+    @property
+    def n_req(self) -> int:
+        return self.spec.n_req
+
+    @property
+    def max_context(self) -> int:
+        return int(self.ctx_final.max())
+
+    def row_slice(self, r: int) -> slice:
+        b = int(self.host_base[r])
+        return slice(b, b + int(self.ctx_final[r]))
+
+
+def _gpu_page_mask(spec: WorkloadSpec, ctx_final: np.ndarray, r: int) -> np.ndarray:
+    """Which logical pages of request r start on GPU (True) vs host."""
+    P = -(-int(ctx_final[r]) // spec.page_size)
+    mask = np.zeros(P, dtype=bool)
+    if spec.residency == "oldest_host":
+        mask[spec.host_pages:] = True
+    elif spec.residency == "mod3":
+        kind = r % 3
+        if kind == 0:
+            mask[:] = True
+        elif kind == 1:
+            n_gpu = math.ceil(0.25 * P)
+            mask[P - n_gpu:] = True
+        # kind 2: none resident
+    elif spec.residency == "budget":
+        n_gpu = min(P, -(-spec.gpu_token_budget // spec.page_size))
+        mask[P - n_gpu:] = True
+    else:
+        raise ValueError(spec.residency)
+    return mask
+
+
+def generate(spec: WorkloadSpec) -> Workload:
+    """Build the host-side inputs of `spec` (rows, residency, placement).
+
+    Scores and queries are drawn step by step with `ScoreStream` and
+    `QueryStream`. Reduced variants for quick tests are plain
+    ``dataclasses.replace`` copies of a spec.
+    """
+    ss = np.random.SeedSequence(spec.seed).spawn(6)
+    gens = {k: np.random.Generator(np.random.PCG64(s)) for k, s in
+            zip(("scores", "rows", "queries", "pages", "contexts", "shifts"), ss)}
+    R = spec.n_req
+    if spec.ctx_range is not None:
+        lo, hi = spec.ctx_range
+        ctx0 = gens["contexts"].integers(lo, hi, endpoint=True, size=R).astype(np.int64)
+    elif spec.growth is not None:
+        ctx0 = np.full(R, spec.growth[0], dtype=np.int64)
+    else:
+        ctx0 = np.full(R, spec.ctx, dtype=np.int64)
+    ctx_final = final_context(spec, ctx0)
+    host_base = np.zeros(R, dtype=np.int64)
+    host_base[1:] = np.cumsum(ctx_final)[:-1]
+    N = int(ctx_final.sum())
+
+    # latent rows, request by request, in chunks of ROW_CHUNK
+    rg = gens["rows"]
+    if spec.kv_dtype == KV_F32:
+        rows = np.empty((N, ROW_DIM), dtype=np.float32)
+    elif spec.kv_dtype == KV_BF16:
+        rows = np.empty((N, ROW_DIM), dtype=np.uint16)
+    else:
+        rows = np.empty((N, ROW_DIM), dtype=np.uint8)
+    scales = np.empty(N, dtype=np.float32) if spec.kv_dtype == KV_FP8 else None
+    for start in range(0, N, ROW_CHUNK):
+        n = min(ROW_CHUNK, N - start)
+        sigma = np.exp(0.5 * rg.standard_normal(n, dtype=np.float32)).astype(np.float32)
+        z = rg.standard_normal((n, ROW_DIM), dtype=np.float32)
+        x = z * sigma[:, None]
+        if spec.kv_dtype == KV_F32:
+            rows[start:start + n] = x
+        elif spec.kv_dtype == KV_BF16:
+            rows[start:start + n] = f32_to_bf16_bits(x)
+        else:
+            c, s = f32_rows_to_fp8(x)
+            rows[start:start + n] = c
+            scales[start:start + n] = s
+
+    # residency and pool placement
+    ps = spec.page_size
+    masks = [_gpu_page_mask(spec, ctx_final, r) for r in range(R)]
+    hot_per_req = spec.hot_rows // ps
+    total = int(sum(m.sum() for m in masks)) + R * hot_per_req
+    perm = gens["pages"].permutation(total).astype(np.int32)
+    cur = 0
+    hot_pages = np.empty((R, hot_per_req), dtype=np.int32)
+    gpu_page = []
+    for r in range(R):
+        hot_pages[r] = perm[cur:cur + hot_per_req]
+        cur += hot_per_req
+        g = np.full(masks[r].size, -1, dtype=np.int32)
+        k = int(masks[r].sum())
+        g[masks[r]] = perm[cur:cur + k]
+        cur += k
+        gpu_page.append(g)
+    wl = Workload(spec=spec, ctx0=ctx0, ctx_final=ctx_final, host_base=host_base,
+                  rows=rows, scales=scales, gpu_page=gpu_page, hot_pages=hot_pages,
+                  num_pool_pages=total, sm_scale=np.float32(1.0 / math.sqrt(ROW_DIM)))
+    wl._streams = gens
+    return wl
+
+
+class ScoreStream:
+    """Per-step indexer scores, [R, max_context] fp32 (zero past each L_r)."""
+
+    def __init__(self, wl: Workload, ctx_sched: Optional[np.ndarray] = None):
+        self.wl = wl
+        self.g = wl._streams["scores"]
+        self.shift_g = wl._streams["shifts"]
+        self.proc = wl.spec.scores
+        self.state: List[Optional[np.ndarray]] = [None] * wl.n_req
+        self.n = 0
+        self.shift_steps: List[int] = []
+
+    def next(self, lens: np.ndarray) -> np.ndarray:
+        """Scores of the next step for context lengths `lens` [R]."""
+        self.n += 1
+        R = self.wl.n_req
+        out = np.zeros((R, self.wl.max_context), dtype=np.float32)
+        kind = self.proc[0]
+        if kind == "iid":
+            for r in range(R):
+                out[r, :lens[r]] = self.g.standard_normal(int(lens[r]), dtype=np.float32)
+            return out
+        rho = np.float32(self.proc[1])
+        sd = np.float32(1.0 / math.sqrt(1.0 - float(rho) ** 2))
+        shift = False
+        if kind == "ar1_shift" and self.n >= 2:
+            shift = bool(self.shift_g.random() < self.proc[2])
+            if shift:
+                self.shift_steps.append(self.n)
+        for r in range(R):
+            L = int(lens[r])
+            prev = self.state[r]
+            if prev is None or shift:
+                s = self.g.standard_normal(L, dtype=np.float32) * sd
+            else:
+                k = min(prev.size, L)
+                s = np.empty(L, dtype=np.float32)
+                s[:k] = rho * prev[:k] + self.g.standard_normal(k, dtype=np.float32)
+                if L > k:  # new tokens start from the stationary law
+                    s[k:] = self.g.standard_normal(L - k, dtype=np.float32) * sd
+            self.state[r] = s
+            out[r, :L] = s
+        return out
+
+
+class QueryStream:
+    """Per-step absorbed queries [R, Q, H, 576]: fp32 array or bf16 bits."""
+
+    def __init__(self, wl: Workload):
+        self.wl = wl
+        self.g = wl._streams["queries"]
+
+    def next(self) -> np.ndarray:
+        s = self.wl.spec
+        q = self.g.standard_normal((s.n_req, s.q_per_req, s.heads, ROW_DIM), dtype=np.float32)
+        if s.q_dtype == "bf16":
+            return f32_to_bf16_bits(q)
+        return q

@@ -1,0 +1,73 @@
+"""The seeded input generator: determinism and the stated structure."""
+import dataclasses
+
+import numpy as np
+
+from sparse_mla_decode_indexer_amd import workload as W
+
+
+def small(name, **kw):
+    return dataclasses.replace(W.SPECS[name], **kw)
+
+
+def test_deterministic_bytes():
+    a = W.generate(small("single-128k", ctx=4096, host_pages=48))
+    b = W.generate(small("single-128k", ctx=4096, host_pages=48))
+    assert np.array_equal(a.rows, b.rows)
+    sa, sb = W.ScoreStream(a), W.ScoreStream(b)
+    for _ in range(3):
+        assert np.array_equal(sa.next(a.ctx0), sb.next(b.ctx0))
+    assert np.array_equal(W.QueryStream(a).next(), W.QueryStream(b).next())
+
+
+def test_residency_and_placement_tiny():
+    wl = W.generate(W.SPECS["tiny"])
+    g = wl.gpu_page[0]
+    assert (g[:48] == -1).all() and (g[48:] >= 0).all() and g.size == 64
+    ids = np.concatenate([g[g >= 0], wl.hot_pages.ravel()])
+    assert np.unique(ids).size == ids.size == wl.num_pool_pages
+    assert wl.rows.dtype == np.float32 and wl.rows.shape == (4096, 576)
+
+
+def test_mod3_states_and_ranges():
+    spec = small("batch32", ctx_range=(1000, 5000))
+    wl = W.generate(spec)
+    for r in range(spec.n_req):
+        g = wl.gpu_page[r]
+        P = g.size
+        if r % 3 == 0:
+            assert (g >= 0).all()
+        elif r % 3 == 1:
+            n_gpu = int(np.ceil(0.25 * P))
+            assert (g[P - n_gpu:] >= 0).all() and (g[:P - n_gpu] == -1).all()
+        else:
+            assert (g == -1).all()
+    assert wl.ctx0.min() >= 1000 and wl.ctx0.max() <= 5000
+
+
+def test_fp8_rows_use_full_range_and_decode_close():
+    from oracle import decode_rows
+    spec = small("single-1m-fp8", ctx=2048, host_pages=29)
+    wl = W.generate(spec)
+    codes = wl.rows
+    # every row reaches |code| = 448 (scale = amax / 448)
+    mags = codes & 0x7F
+    assert (mags.max(axis=1) == 0x7E).all()
+    x = decode_rows(codes[:4], wl.scales[:4], "fp8")
+    assert np.isfinite(x).all()
+
+
+def test_ar1_stationary_variance():
+    spec = small("single-128k", ctx=65536, host_pages=768)
+    wl = W.generate(spec)
+    ss = W.ScoreStream(wl)
+    v = [ss.next(wl.ctx0)[0].var() for _ in range(3)]
+    assert all(abs(x - 1 / (1 - 0.81)) < 0.2 for x in v)
+
+
+def test_agent_schedule():
+    sched = W.context_schedule(W.SPECS["agent16"], np.full(16, 74160), 715)
+    assert sched[0, 0] == 74160 and sched[54, 0] == 74160 + 54 * 4
+    assert sched[55, 0] == 74160 + 220 + 753
+    assert sched[-1, 0] == 86056 - 4
+    assert W.final_context(W.SPECS["agent16"], np.array([74160]))[0] == 86056
