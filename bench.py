@@ -1,0 +1,235 @@
+"""Benchmark: tiered sparse-MLA decode steps on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload single-128k]
+
+A step is the whole hot path for every request of the workload: top-K over
+the indexer scores -> fused resolve (resident / hot / miss copy over PCIe)
+-> sparse MLA attention over the K resolved rows. Inputs (scores and
+queries of every step) are resident in HBM before timing; the K timed
+steps are one hipGraph replay, bracketed by HIP events on the replay
+stream. Prints one JSON line.
+
+Roofline: the same K steps are replayed again from a snapshot of the
+pool state, with HIP events around each of the three entry points (a spin
+kernel first lets the host queue run ahead, so the events see GPU time
+only). The entry point with the largest average duration is reported
+against its bound (PCIe for the miss copy, HBM for the scans and gathers)
+with its algorithmic bytes per launch.
+
+cpu_baseline: the CPU oracle (tests' reference, fp64 numpy) timed on a
+bounded prefix of the same steps on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+PCIE_PEAK_GBS = 64.0         # PCIe 5.0 x16, one direction, published
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="single-128k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-roofline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); requests are independent "
+              "and shard by request with no exchange, so a multi-GPU figure is not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_mla_decode_indexer_amd import harness as Hn
+    from sparse_mla_decode_indexer_amd import workload as W
+
+    spec = W.SPECS[args.workload]
+    K, Wm = args.steps, args.warmup
+    T = K + Wm
+    wl = W.generate(spec)
+    if spec.growth is not None and T > spec.steps:
+        raise SystemExit(f"{spec.name} defines {spec.steps} steps")
+    sched = W.context_schedule(spec, wl.ctx0, T) if spec.growth is not None else \
+        np.broadcast_to(wl.ctx0, (T, spec.n_req))
+    if spec.growth is not None:
+        raise SystemExit("growing-context workloads are parity cases, not bench lines")
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    pool = Hn.make_pool(wl, device=dev)
+    Hn.load_workload(pool, wl)
+    buf = Hn.StepBuffers(wl, device=dev, n_steps=T)
+    ss, qs = W.ScoreStream(wl), W.QueryStream(wl)
+    host_scores, host_q = [], []
+    for n in range(T):
+        sc, q = ss.next(sched[n]), qs.next()
+        buf.upload(n, sc, q)
+        if n < 64 and sc.nbytes * (n + 1) < (1 << 30):
+            host_scores.append(sc)
+            host_q.append(q)
+    torch.cuda.synchronize()
+    print(f"[bench] {spec.name}: inputs resident, {T} steps", file=sys.stderr, flush=True)
+
+    # warmup: W eager steps
+    for n in range(Wm):
+        Hn.decode_step(pool, buf, n)
+    torch.cuda.synchronize()
+
+    # capture the K timed steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for n in range(Wm, T):
+            Hn.decode_step(pool, buf, n)
+    torch.cuda.synchronize()
+    snap_state = pool.state.clone()
+    snap_rows = pool.pool_rows.clone()
+    snap_scales = None if pool.pool_scales is None else pool.pool_scales.clone()
+    views = pool.state_views()
+    c0 = views["counters"].clone()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / K
+    dc = (views["counters"] - c0).cpu().numpy().sum(axis=0)  # resident, hot, miss over K steps
+    code = pool.device_error()
+    if code[0] != 0:
+        raise SystemExit(f"device error {code}")
+    print(f"[bench] timed {K} steps: {ms:.3f} ms", file=sys.stderr, flush=True)
+
+    R, Kt, S = spec.n_req, spec.top_k, spec.hot_rows
+    rb = W.row_bytes(spec.kv_dtype) + (4 if spec.kv_dtype == "fp8" else 0)
+    lens = np.asarray(wl.ctx0, dtype=np.int64)
+    rows_per_step = int(np.minimum(Kt, lens).sum())
+    misses_per_step = dc[2] / K
+    qb = 4 if spec.q_dtype == "f32" else 2
+    QH = spec.q_per_req * spec.heads
+    # algorithmic bytes of one step (what the method must move)
+    b_topk = 4 * lens.sum() + 4 * R * Kt
+    b_resolve_hbm = R * (12 * Kt + 8 * S) + misses_per_step * rb
+    b_pcie = misses_per_step * rb
+    b_attn = rows_per_step * rb + R * QH * (576 * qb + 512 * 4 + 4) + 4 * R * Kt
+    flops_attn = 2.0 * QH * rows_per_step * (576 + 512)
+
+    roof = None
+    if not args.no_roofline:
+        pool.state.copy_(snap_state)
+        pool.pool_rows.copy_(snap_rows)
+        if snap_scales is not None:
+            pool.pool_scales.copy_(snap_scales)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        torch.cuda._sleep(int(2e8))  # let the host queue run ahead of the GPU
+        for j, n in enumerate(range(Wm, T)):
+            ev = evs[j]
+            ev[0].record(stream)
+            pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
+            ev[1].record(stream)
+            pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
+            ev[2].record(stream)
+            pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)
+            ev[3].record(stream)
+        torch.cuda.synchronize()
+        dur = np.array([[ev[a].elapsed_time(ev[a + 1]) for a in range(3)] for ev in evs])  # ms
+        avg = dur.mean(axis=0) * 1e3  # us
+        names = ["select_topk", "resolve_rows", "sparse_mla_decode"]
+        per = {
+            "select_topk": dict(bound="hbm", bytes=b_topk, peak=HBM_PEAK_GBS),
+            "resolve_rows": dict(bound="pcie", bytes=b_pcie, peak=PCIE_PEAK_GBS),
+            "sparse_mla_decode": dict(bound="hbm", bytes=b_attn, peak=HBM_PEAK_GBS),
+        }
+        dom = int(np.argmax(avg))
+        name = names[dom]
+        d = per[name]
+        achieved = d["bytes"] / (avg[dom] * 1e-6) / 1e9
+        roof = {"kernel": name, "bound": d["bound"], "achieved": round(achieved, 2),
+                "peak": d["peak"], "unit": "GB/s", "frac": round(achieved / d["peak"], 4),
+                "traffic": None,
+                "avg_us": {n: round(float(a), 2) for n, a in zip(names, avg)},
+                "bytes_per_launch": {n: int(per[n]["bytes"]) for n in names},
+                "attention_tflops": round(flops_attn / (avg[2] * 1e-6) / 1e12, 2)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, host_scores, host_q, sched, args.cpu_seconds)
+
+    step_hbm = b_topk + b_resolve_hbm + b_attn
+    value = 1e3 / ms_per_step
+    line = {
+        "metric": "sparse-MLA decode steps/s + top-K rows resolved/s; % of HBM/PCIe roofline",
+        "value": round(value, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8e4m3+bf16"}[spec.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": R, "context": int(lens.max()),
+                   "kv_dtype": spec.kv_dtype, "heads": spec.heads, "q_per_req": spec.q_per_req,
+                   "top_k": Kt, "hot_rows": S, "residency": spec.residency},
+        "rows_resolved_per_s": round(rows_per_step * value, 1),
+        "misses_per_step": round(float(misses_per_step), 1),
+        "hits_per_step": round(float(dc[1] / K), 1),
+        "resident_per_step": round(float(dc[0] / K), 1),
+        "step_hbm_frac": round(step_hbm / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+        "step_pcie_frac": round(b_pcie / (ms_per_step * 1e-3) / 1e9 / PCIE_PEAK_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    pool.close()
+    print(json.dumps(line))
+
+
+def cpu_baseline(wl, host_scores, host_q, sched, budget_s):
+    """Time the CPU oracle (full step: top-K, LRU, fp64 attention) on the
+    first steps of the same inputs until the budget is spent."""
+    from oracle import DecodeOracle, bf16_decode
+
+    s = wl.spec
+    orc = DecodeOracle(rows=wl.rows, scales=wl.scales, kv_dtype=s.kv_dtype, host_base=wl.host_base,
+                       gpu_page=wl.gpu_page, hot_pages=wl.hot_pages, page_size=s.page_size,
+                       top_k=s.top_k, hot_rows=s.hot_rows, ctx_capacity=wl.ctx_final,
+                       sm_scale=wl.sm_scale)
+    t0 = time.perf_counter()
+    n = 0
+    while n < len(host_scores) and time.perf_counter() - t0 < budget_s:
+        q = host_q[n]
+        qd = bf16_decode(q) if q.dtype == np.uint16 else q.astype(np.float64)
+        orc.step(host_scores[n], qd, sched[n], with_attention=True)
+        n += 1
+    el = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(n / el, 3), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} decode steps of {s.name} (top-K sort, LRU simulation, fp64 "
+                      f"attention over all heads), numpy with up to {cores} BLAS threads",
+            "seconds": round(el, 2)}
+
+
+if __name__ == "__main__":
+    main()

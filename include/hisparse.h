@@ -1,0 +1,263 @@
+/*
+ * hisparse.h — C ABI of the tiered sparse-MLA decode step (libhisparse.so).
+ *
+ * One decode step of one sparse-MLA layer over a latent KV cache whose pages
+ * live either in GPU memory or only in pinned host memory:
+ *   hs_select_topk      the indexer's top-K over per-token scores;
+ *   hs_resolve_rows     one fused pass that turns each selected token into a
+ *                       physical pool row: read in place when its page is on
+ *                       the GPU, read from the request's hot buffer (and its
+ *                       LRU entry refreshed) when it is hot, or, on a miss,
+ *                       copy that single row from pinned host memory into
+ *                       the least-recently-used hot slot;
+ *   hs_sparse_mla_decode absorbed-MLA decode attention over only those rows.
+ *
+ * Pages describing the method (cited by title and section):
+ *   [P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" (agentlenshq.com)
+ *   [P3] "vLLM Hybrid HiSparse：稀疏MLA破解长上下文显存瓶颈" (kongchang.com)
+ *
+ * Conventions shared by every call
+ *   - Every call returns an hs_status; nothing throws across the ABI.
+ *   - The per-step calls (select_topk, resolve_rows, sparse_mla_decode) and
+ *     set_residency only enqueue kernels on the given stream. They never
+ *     allocate, never synchronise and never read device memory from the
+ *     host, so a caller may capture them in a hipGraph. Their arguments are
+ *     validated on the host before anything is enqueued; on an error return
+ *     nothing was enqueued.
+ *   - Data errors that only the device can see (a selected index past the
+ *     context length, a page id outside the pool, a plan row outside the
+ *     pool) set a sticky device error word (first error wins) and the
+ *     offending entry is treated as absent. Read it with
+ *     hs_get_device_error (not capturable).
+ *   - Ownership: the caller allocates every device buffer (pool rows, fp8
+ *     scales, the state workspace, inputs and outputs) and keeps it alive
+ *     until hs_destroy_pool. The library owns only its host-side handle and
+ *     the pinned host row store, which it allocates in hs_init_pool.
+ *   - A pool handle is not thread-safe; calls on one pool must be ordered
+ *     on one stream (or synchronised by the caller across streams).
+ *   - All element indices are int32 unless stated; host store rows int64.
+ */
+#ifndef HISPARSE_H_
+#define HISPARSE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;  /* HIP stream handle (NULL = null stream) */
+typedef struct hs_pool hs_pool;            /* opaque pool handle */
+
+typedef enum hs_status {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or out-of-range id */
+  HS_ERR_CAPACITY = 2,         /* exceeds what the pool was built for (e.g. hot_rows < top_k) */
+  HS_ERR_UNSUPPORTED = 3,      /* dtype or shape combination not implemented */
+  HS_ERR_HIP = 4,              /* a HIP runtime call failed; see hs_last_hip_error */
+  HS_ERR_OUT_OF_MEMORY = 5,    /* the pinned host store could not be allocated */
+  HS_ERR_DEVICE = 6            /* hs_get_device_error found a device-side data error */
+} hs_status;
+
+typedef enum hs_dtype {
+  HS_F32 = 0,       /* IEEE fp32 */
+  HS_BF16 = 1,      /* bfloat16 */
+  HS_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn", max 448), with one fp32 scale per row */
+} hs_dtype;
+
+/* Device error word codes (hs_get_device_error). */
+enum {
+  HS_DEV_OK = 0,
+  HS_DEV_INDEX_RANGE = 1,  /* a selected token >= the request's context length */
+  HS_DEV_PAGE_RANGE = 2,   /* a page-table or hot-page id >= num_pool_pages */
+  HS_DEV_PLAN_RANGE = 3,   /* an attention plan row >= the pool's row count */
+  HS_DEV_REQUEST_RANGE = 4 /* a req_ids entry outside [0, max_requests) */
+};
+
+/* hs_set_residency flags */
+enum { HS_RESET_HOT = 1u /* empty the request's hot buffer (nothing hot) */ };
+
+/*
+ * Pool description. The latent row layout is MLA's: nope_dim (512) dims that
+ * serve as the value and nope_dim + rope_dim (576) dims that serve as the key
+ * ([P3] §"稀疏MLA的核心思想", MLA note). Tokens are grouped in pages of
+ * page_size rows ([P3] PagedAttention note). Each request's hot buffer is
+ * hot_rows slots made of ordinary pool pages leased to it
+ * ([P2] §"关键架构细节", first bullet; [P3] §"复用现有内存池"); hot_rows = 0
+ * selects the default 2 x top_k.
+ */
+typedef struct hs_pool_desc {
+  int32_t page_size;      /* tokens per page: power of two in [1, 1024] */
+  int32_t num_pool_pages; /* device pool pages (resident pages + leased hot pages) */
+  int32_t max_requests;   /* request ids are 0 .. max_requests-1 */
+  int32_t max_context;    /* most tokens any request holds, >= 1 */
+  int32_t nope_dim;       /* must be 512 */
+  int32_t rope_dim;       /* must be 64 */
+  int32_t kv_dtype;       /* hs_dtype of the stored rows */
+  int32_t top_k;          /* K: 1 .. 4096 */
+  int32_t hot_rows;       /* S per request; 0 -> 2*top_k; must be >= top_k,
+                             <= 8192 and a multiple of page_size */
+  int32_t max_batch;      /* most requests in one per-step call, 1 .. max_requests */
+  int32_t max_q_rows;     /* most q_per_req * n_heads in one sparse_mla_decode call */
+  int32_t reserved0;      /* must be 0 */
+  int64_t host_rows;      /* rows in the pinned host store, >= 1 */
+} hs_pool_desc;
+
+/* Sizes the caller must provide, derived from a descriptor. */
+typedef struct hs_pool_sizes {
+  size_t row_bytes;          /* bytes of one stored row payload: 2304 f32, 1152 bf16, 576 fp8 */
+  size_t pool_bytes;         /* device pool rows: num_pool_pages * page_size * row_bytes */
+  size_t pool_scale_bytes;   /* fp8 only: 4 * pool rows (one fp32 scale per row); else 0 */
+  size_t state_bytes;        /* device state workspace (tables, LRU state, scratch) */
+  size_t host_store_bytes;   /* pinned host memory hs_init_pool allocates */
+  int32_t hot_rows;          /* resolved S */
+  int32_t pages_per_request; /* ceil(max_context / page_size) */
+} hs_pool_sizes;
+
+/* Byte offsets of the state arrays inside the caller's workspace, so that a
+ * caller can inspect (never write) the residency and LRU state. */
+typedef struct hs_state_layout {
+  size_t ctx_len;     /* int32 [max_requests]: context length L_r */
+  size_t host_base;   /* int64 [max_requests]: host store row of token 0 */
+  size_t page_table;  /* int32 [max_requests][pages_per_request]: pool page or -1 (host only) */
+  size_t hot_pages;   /* int32 [max_requests][hot_rows/page_size]: leased pool pages */
+  size_t rev;         /* int32 [max_requests][max_context]: hot slot holding token t, or -1 */
+  size_t slot_tag;    /* int32 [max_requests][hot_rows]: token in slot s, or -1 */
+  size_t slot_stamp;  /* int32 [max_requests][hot_rows]: step of last hit or fill, 0 = never */
+  size_t lru_order;   /* int32 [max_requests][hot_rows]: slots by ascending (stamp, slot) */
+  size_t step;        /* int32 [max_requests]: resolves done so far */
+  size_t counters;    /* int64 [max_requests][3]: cumulative resident, hot, miss */
+  size_t error;       /* uint32 [4]: code, request, index, 0 */
+  size_t scratch;     /* start of internal scratch */
+  size_t total;       /* == hs_pool_sizes.state_bytes */
+} hs_state_layout;
+
+/* Derive buffer sizes from a descriptor. Pure host computation.
+ * Errors: INVALID_ARGUMENT (null or malformed descriptor), CAPACITY
+ * (hot_rows < top_k), UNSUPPORTED (dims other than 512 + 64). */
+hs_status hs_pool_requirements(const hs_pool_desc* desc, hs_pool_sizes* out);
+
+/* Create a pool over caller-owned device memory.
+ *   pool_rows    device, >= pool_bytes, row r at byte offset r * row_bytes;
+ *                physical row r = page * page_size + offset-in-page
+ *   pool_scales  device fp32 [pool rows] for HS_FP8_E4M3, else NULL
+ *   state        device workspace, >= state_bytes, 256-byte aligned
+ * Allocates the pinned host row store (host_rows rows of row_bytes, plus
+ * fp32 scales for fp8), mapped for direct device reads over PCIe, and
+ * enqueues the state initialisation on `stream` (every page host-only, every
+ * hot buffer empty, counters and the error word zero). *out receives the
+ * handle. Errors: those of hs_pool_requirements, INVALID_ARGUMENT (null or
+ * misaligned pointer, state_bytes too small), OUT_OF_MEMORY, HIP. */
+hs_status hs_init_pool(const hs_pool_desc* desc, void* pool_rows, float* pool_scales,
+                       void* state, size_t state_bytes, hipStream_t stream, hs_pool** out);
+
+/* Pinned host store of the pool ([P2] §"混合 HiSparse 的技术实现", state 2:
+ * misses are copied from pinned host memory). *rows: host_rows x row_bytes,
+ * row-major; *scales: fp32 [host_rows] for fp8 pools, else NULL. The caller
+ * fills it (the store keeps a copy of every row, so any page can be
+ * demoted at any time). Errors: INVALID_ARGUMENT. */
+hs_status hs_host_rows(hs_pool* pool, void** rows, float** scales);
+
+/* Set request `req`'s context length and page residency (stream-ordered).
+ *   context_len    L_r, 0 .. max_context
+ *   host_row_base  host store row holding token 0; tokens 0..L_r-1 map to
+ *                  rows host_row_base .. host_row_base + L_r - 1
+ *   first_page, num_pages, gpu_page_ids
+ *                  device int32 [num_pages]: the pool page holding logical
+ *                  page first_page + i, or -1 when it lives only on host
+ *                  ([P2] §"混合 HiSparse 的技术实现": residency is tracked
+ *                  per page). num_pages may be 0 (gpu_page_ids then unused).
+ *   hot_page_ids   device int32 [hot_rows/page_size]: pool pages leased as the
+ *                  request's hot buffer, or NULL to keep the current lease
+ *                  (must be given once before the first resolve)
+ *   flags          HS_RESET_HOT empties the hot buffer ([P2] state 3: a
+ *                  request that starts host-only loads rows only on demand)
+ * No hot invalidation is needed when pages move: a page that is back on GPU
+ * is read in place before any stale hot copy. Errors: INVALID_ARGUMENT. */
+hs_status hs_set_residency(hs_pool* pool, int32_t req, int32_t context_len,
+                           int64_t host_row_base, int32_t first_page, int32_t num_pages,
+                           const int32_t* gpu_page_ids, const int32_t* hot_page_ids,
+                           uint32_t flags, hipStream_t stream);
+
+/* Indexer top-K ([P3] §"稀疏MLA的核心思想": decode attends only to the
+ * top-K tokens; [P2] §"解决 KV 缓存内存压力"). For each i < n_req, with
+ * r = req_ids[i] (device int32 [n_req]) and L = L_r read on the device:
+ * writes idx_out[i][0..top_k) (device int32) = the min(top_k, L) token
+ * indices with the largest scores[i * score_stride + t], t < L; equal scores
+ * keep the lower index; -0.0 equals +0.0; listed in ascending index order,
+ * padded with -1. NaN scores are not supported. scores: device fp32, 16-byte
+ * aligned, row i valid over its first L entries; score_stride >= max_context
+ * and a multiple of 4.
+ * Errors: INVALID_ARGUMENT, CAPACITY (n_req > max_batch). */
+hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_stride,
+                         const int32_t* req_ids, int32_t n_req, int32_t* idx_out,
+                         hipStream_t stream);
+
+/* Fused resolve ([P2] §"混合 HiSparse 的技术实现", state 2: one fused kernel
+ * handles the top-K results — resident rows read in place, hot rows read and
+ * their LRU entry refreshed, a miss copies the single row from pinned host
+ * memory into the LRU slot; [P3] §"融合内核与CUDA图兼容"). For each i < n_req
+ * (request r = req_ids[i]), over idx[i][0..top_k) (device int32, ascending,
+ * -1 padded, as hs_select_topk writes it):
+ *   - classify each token t: RESIDENT if its page is on GPU, else HOT if a
+ *     hot slot holds it, else MISS;
+ *   - every HOT slot gets stamp n (this request's n-th resolve);
+ *   - the misses, in ascending token order, take the slots not touched this
+ *     step in ascending (stamp, slot) order; an evicted token loses its slot;
+ *     each miss's row (and fp8 scale) is copied from the host store into its
+ *     slot's pool row;
+ *   - plan_out[i][j] (device int32 [n_req][top_k]) = the physical pool row
+ *     holding token idx[i][j] (page * page_size + offset for RESIDENT, the
+ *     slot's leased row otherwise), -1 for padding;
+ *   - counts_out[i] (device int32 [n_req][3], may be NULL) = resident, hot,
+ *     miss counts; they sum to min(top_k, L_r).
+ * Each request's step counter advances by one. A request must appear at most
+ * once per call. Errors: INVALID_ARGUMENT, CAPACITY. */
+hs_status hs_resolve_rows(hs_pool* pool, const int32_t* idx, const int32_t* req_ids,
+                          int32_t n_req, int32_t* plan_out, int32_t* counts_out,
+                          hipStream_t stream);
+
+/* Sparse MLA decode attention over the resolved rows ([P3] §"稀疏MLA的核心思想"
+ * and its MLA note; [P2] §"与 vLLM 栈的集成", speculative decoding: one
+ * resolve plan is replayed for all query tokens of a request).
+ *   q        device [n_req][q_per_req][n_heads][576], q_dtype HS_F32 (pool
+ *            HS_F32) or HS_BF16 (pool HS_BF16 or HS_FP8_E4M3)
+ *   plan     device int32 [n_req][top_k] from hs_resolve_rows (-1 = absent)
+ *   out      device fp32 [n_req][q_per_req][n_heads][512]:
+ *            out = sum_j softmax_j(sm_scale * <q, row_j>) * row_j[0:512]
+ *            over the present rows j (fp8 rows are code * row scale)
+ *   lse_out  device fp32 [n_req][q_per_req][n_heads] = log sum_j exp(...), or NULL
+ * With no present rows the output is 0 and lse is -inf.
+ * Errors: INVALID_ARGUMENT, CAPACITY (n_req > max_batch or
+ * q_per_req * n_heads > max_q_rows), UNSUPPORTED (dtype combination). */
+hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype,
+                               int32_t n_req, int32_t q_per_req, int32_t n_heads,
+                               const int32_t* plan, float sm_scale, float* out,
+                               float* lse_out, hipStream_t stream);
+
+/* Byte offsets of the state arrays in the workspace. Errors: INVALID_ARGUMENT. */
+hs_status hs_get_state_layout(const hs_pool* pool, hs_state_layout* out);
+
+/* Synchronise `stream`, then read the sticky device error word into
+ * code[0..3] (code, request, index, 0). Returns HS_ERR_DEVICE when code[0] != 0.
+ * Not capturable. Errors: INVALID_ARGUMENT, HIP, DEVICE. */
+hs_status hs_get_device_error(hs_pool* pool, uint32_t code[4], hipStream_t stream);
+
+/* Clear the sticky device error word (stream-ordered). */
+hs_status hs_clear_device_error(hs_pool* pool, hipStream_t stream);
+
+/* The hipError_t value of the last failing HIP call on this thread. */
+int32_t hs_last_hip_error(void);
+
+/* Static text for a status code. */
+const char* hs_status_string(hs_status status);
+
+/* Free the pinned host store and the handle. Device buffers stay the
+ * caller's. Synchronises the device first. NULL is a no-op. */
+hs_status hs_destroy_pool(hs_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HISPARSE_H_ */

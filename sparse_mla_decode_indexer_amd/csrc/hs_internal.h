@@ -1,0 +1,146 @@
+// Internal declarations of libhisparse: the pool handle, the workspace
+// layout, device-side helpers shared by the kernels, and the launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hs {
+
+// ---------------------------------------------------------------- constants
+constexpr int kRowDim = 576;       // 512 nope + 64 rope
+constexpr int kNope = 512;
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxHotRows = 8192;
+
+// top-K: one workgroup scans one chunk of kTkChunk scores
+constexpr int kTkChunk = 2048;
+constexpr int kTkThreads = 256;
+constexpr int kTkBins = 4096;      // 12-bit radix digits
+constexpr int kTkFinalThreads = 1024;
+constexpr int kTkMaxChunks = 2048; // => max_context <= 4,194,304
+
+// resolve
+constexpr int kRsThreads = 1024;
+constexpr int kCopyThreads = 256;
+
+// attention
+constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)
+
+// ---------------------------------------------------------------- the handle
+struct Offsets {
+  size_t tk_hist, tk_done, tk_sel, tk_count, tk_cand;
+  size_t rs_miss_count, rs_miss_src, rs_miss_dst;
+  size_t at_part_o, at_part_lse;
+  int64_t at_part_rows;  // capacity of partial rows
+};
+
+}  // namespace hs
+
+struct hs_pool {
+  hs_pool_desc d;
+  hs_pool_sizes sz;
+  hs_state_layout lay;
+  hs::Offsets off;
+  int device;
+  int log2_ps;
+  int64_t pool_rows_n;        // num_pool_pages * page_size
+  uint8_t* pool_rows;         // device
+  float* pool_scales;         // device (fp8) or null
+  uint8_t* state;             // device workspace
+  void* host_rows;            // pinned, mapped
+  float* host_scales;         // pinned, mapped (fp8) or null
+};
+
+namespace hs {
+
+// Typed views of the workspace, passed by value to kernels.
+struct StateView {
+  int32_t* ctx_len;
+  int64_t* host_base;
+  int32_t* page_table;
+  int32_t* hot_pages;
+  int32_t* rev;
+  int32_t* slot_tag;
+  int32_t* slot_stamp;
+  int32_t* lru_order;
+  int32_t* step;
+  int64_t* counters;
+  uint32_t* error;
+  int32_t max_requests, max_context, pages_per_req, hot_rows, hot_pages_per_req;
+  int32_t page_size, log2_ps, num_pool_pages, top_k;
+};
+
+StateView make_view(const hs_pool* p);
+hs_status set_hip_error(hipError_t e);
+
+#define HS_HIP_CHECK(expr)                         \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hs::set_hip_error(e_); \
+  } while (0)
+
+hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
+                      int32_t n_req, int32_t* idx_out, hipStream_t s);
+hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
+                         int32_t* plan_out, int32_t* counts_out, hipStream_t s);
+hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
+                           int32_t q_per_req, int32_t n_heads, const int32_t* plan,
+                           float sm_scale, float* out, float* lse_out, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+// Sticky device error word: the first error wins; later ones are dropped.
+__device__ inline void raise_error(uint32_t* err, uint32_t code, uint32_t a, uint32_t b) {
+  if (atomicCAS(err, 0u, code) == 0u) {
+    err[1] = a;
+    err[2] = b;
+  }
+}
+
+// Exclusive prefix count of a per-thread flag over the whole block, in
+// thread order. `tmp` holds one int per wave (blockDim.x / 64 entries) plus
+// one; the block total is returned in `total`. Contains two barriers.
+__device__ inline int block_excl_count(bool f, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const unsigned long long m = __ballot(f);
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) tmp[wave] = __popcll(m);
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = tmp[w];
+    pre += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + below;
+}
+
+// Exclusive prefix sum of a per-thread int over the block, in thread order.
+__device__ inline int block_excl_sum(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = tmp[w];
+    pre += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
+}  // namespace hs

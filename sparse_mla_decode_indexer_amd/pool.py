@@ -1,0 +1,120 @@
+"""TieredPool: torch owns the device buffers, libhisparse does the work.
+
+Marshalling only: this class allocates the caller-owned device buffers the
+C ABI asks for (pool rows, fp8 scales, state workspace) with torch, exposes
+the pinned host store as numpy arrays, and forwards each call to the
+library on torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+ROW_DIM, NOPE = 576, 512
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class TieredPool:
+    def __init__(self, *, page_size: int, num_pool_pages: int, max_requests: int, max_context: int,
+                 kv_dtype: str, top_k: int, hot_rows: int = 0, max_batch: Optional[int] = None,
+                 max_q_rows: int = 128, host_rows: int, device: str = "cuda"):
+        self.desc = B.HsPoolDesc(page_size=page_size, num_pool_pages=num_pool_pages,
+                                 max_requests=max_requests, max_context=max_context, nope_dim=512,
+                                 rope_dim=64, kv_dtype=B.DTYPE_CODES[kv_dtype], top_k=top_k,
+                                 hot_rows=hot_rows, max_batch=max_batch or max_requests,
+                                 max_q_rows=max_q_rows, reserved0=0, host_rows=host_rows)
+        self.kv_dtype = kv_dtype
+        self.sizes = B.pool_requirements(self.desc)
+        self.device = torch.device(device)
+        self.row_bytes = int(self.sizes.row_bytes)
+        self.n_pool_rows = num_pool_pages * page_size
+        self.pool_rows = torch.empty(int(self.sizes.pool_bytes), dtype=torch.uint8, device=self.device)
+        self.pool_scales = (torch.zeros(self.n_pool_rows, dtype=torch.float32, device=self.device)
+                            if kv_dtype == "fp8" else None)
+        self.state = torch.empty(int(self.sizes.state_bytes), dtype=torch.uint8, device=self.device)
+        assert self.state.data_ptr() % 256 == 0
+        self.handle = B.init_pool(self.desc, self.pool_rows.data_ptr(), _ptr(self.pool_scales),
+                                  self.state.data_ptr(), int(self.sizes.state_bytes), _stream())
+        rows_p, scales_p = B.host_rows(self.handle)
+        n = host_rows * self.row_bytes
+        self.host_store = np.ctypeslib.as_array((ctypes.c_uint8 * n).from_address(rows_p)).reshape(
+            host_rows, self.row_bytes)
+        self.host_scales = (np.ctypeslib.as_array((ctypes.c_float * host_rows).from_address(scales_p))
+                            if kv_dtype == "fp8" else None)
+        self.layout = B.get_state_layout(self.handle)
+        self.hot_rows = int(self.sizes.hot_rows)
+        self.pages_per_request = int(self.sizes.pages_per_request)
+
+    # ------------------------------------------------------------ views
+    def pool_row_view(self) -> torch.Tensor:
+        return self.pool_rows.view(self.n_pool_rows, self.row_bytes)
+
+    def state_views(self) -> Dict[str, torch.Tensor]:
+        d, L = self.desc, self.layout
+        R, S = d.max_requests, self.hot_rows
+
+        def v(off, dtype, *shape):
+            n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+            return self.state[off:off + n].view(dtype).view(*shape)
+        return {
+            "ctx_len": v(L.ctx_len, torch.int32, R),
+            "host_base": v(L.host_base, torch.int64, R),
+            "page_table": v(L.page_table, torch.int32, R, self.pages_per_request),
+            "hot_pages": v(L.hot_pages, torch.int32, R, S // d.page_size),
+            "rev": v(L.rev, torch.int32, R, d.max_context),
+            "slot_tag": v(L.slot_tag, torch.int32, R, S),
+            "slot_stamp": v(L.slot_stamp, torch.int32, R, S),
+            "lru_order": v(L.lru_order, torch.int32, R, S),
+            "step": v(L.step, torch.int32, R),
+            "counters": v(L.counters, torch.int64, R, 3),
+            "error": v(L.error, torch.int32, 4),
+        }
+
+    # ------------------------------------------------------------ calls
+    def set_residency(self, req: int, context_len: int, host_row_base: int,
+                      gpu_page_ids: Optional[torch.Tensor], first_page: int = 0,
+                      hot_page_ids: Optional[torch.Tensor] = None, reset_hot: bool = False):
+        n = 0 if gpu_page_ids is None else int(gpu_page_ids.numel())
+        B.set_residency(self.handle, req, context_len, host_row_base, first_page, n,
+                        _ptr(gpu_page_ids), _ptr(hot_page_ids), B.HS_RESET_HOT if reset_hot else 0,
+                        _stream())
+
+    def select_topk(self, scores: torch.Tensor, req_ids: torch.Tensor, idx_out: torch.Tensor):
+        B.select_topk(self.handle, scores.data_ptr(), scores.stride(0), req_ids.data_ptr(),
+                      int(req_ids.numel()), idx_out.data_ptr(), _stream())
+
+    def resolve_rows(self, idx: torch.Tensor, req_ids: torch.Tensor, plan_out: torch.Tensor,
+                     counts_out: Optional[torch.Tensor] = None):
+        B.resolve_rows(self.handle, idx.data_ptr(), req_ids.data_ptr(), int(req_ids.numel()),
+                       plan_out.data_ptr(), _ptr(counts_out), _stream())
+
+    def sparse_mla_decode(self, q: torch.Tensor, plan: torch.Tensor, sm_scale: float,
+                          out: torch.Tensor, lse: Optional[torch.Tensor] = None):
+        n_req, q_per_req, n_heads, _ = q.shape
+        qd = B.HS_F32 if q.dtype == torch.float32 else B.HS_BF16
+        B.sparse_mla_decode(self.handle, q.data_ptr(), qd, n_req, q_per_req, n_heads, plan.data_ptr(),
+                            sm_scale, out.data_ptr(), _ptr(lse), _stream())
+
+    def device_error(self):
+        return B.get_device_error(self.handle, _stream())
+
+    def clear_device_error(self):
+        B.clear_device_error(self.handle, _stream())
+
+    def close(self):
+        if self.handle:
+            B.destroy_pool(self.handle)
+            self.handle = 0
+            self.host_store = self.host_scales = None

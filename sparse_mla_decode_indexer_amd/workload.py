@@ -21,7 +21,8 @@ Recipe (all draws seeded; every array is produced once on the host):
   * master seed = 20261202 + c for workload c in 1..5;
     ``numpy.random.SeedSequence(seed).spawn(6)`` gives independent streams
     for scores, rows, queries, page placement, context lengths and topic
-    shifts;
+    shifts; the rows stream is split again per request and per chunk of
+    65,536 rows;
   * latent row t: x = sigma_t * z, z ~ N(0,1)^576, sigma_t = exp(0.5*N(0,1))
     (per-row log-normal magnitude so per-row fp8 scales differ); stored as
     fp32, bf16 (round-to-nearest-even) or OCP fp8 e4m3fn codes with one fp32
@@ -37,8 +38,10 @@ Recipe (all draws seeded; every array is produced once on the host):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -252,8 +255,9 @@ def generate(spec: WorkloadSpec) -> Workload:
     host_base[1:] = np.cumsum(ctx_final)[:-1]
     N = int(ctx_final.sum())
 
-    # latent rows, request by request, in chunks of ROW_CHUNK
-    rg = gens["rows"]
+    # latent rows: request r, chunk c (ROW_CHUNK rows) draws from its own
+    # stream rows_seq.spawn(R)[r].spawn(n_chunks_r)[c], so chunks can be
+    # generated in parallel
     if spec.kv_dtype == KV_F32:
         rows = np.empty((N, ROW_DIM), dtype=np.float32)
     elif spec.kv_dtype == KV_BF16:
@@ -261,19 +265,30 @@ def generate(spec: WorkloadSpec) -> Workload:
     else:
         rows = np.empty((N, ROW_DIM), dtype=np.uint8)
     scales = np.empty(N, dtype=np.float32) if spec.kv_dtype == KV_FP8 else None
-    for start in range(0, N, ROW_CHUNK):
-        n = min(ROW_CHUNK, N - start)
-        sigma = np.exp(0.5 * rg.standard_normal(n, dtype=np.float32)).astype(np.float32)
-        z = rg.standard_normal((n, ROW_DIM), dtype=np.float32)
-        x = z * sigma[:, None]
+    tasks = []
+    for r, rss in enumerate(ss[1].spawn(R)):
+        n_r = int(ctx_final[r])
+        nch = -(-n_r // ROW_CHUNK)
+        for c, css in enumerate(rss.spawn(nch)):
+            start = int(host_base[r]) + c * ROW_CHUNK
+            tasks.append((css, start, min(ROW_CHUNK, n_r - c * ROW_CHUNK)))
+
+    def fill(task):
+        css, start, n = task
+        g = np.random.Generator(np.random.PCG64(css))
+        sigma = np.exp(0.5 * g.standard_normal(n, dtype=np.float32)).astype(np.float32)
+        x = g.standard_normal((n, ROW_DIM), dtype=np.float32) * sigma[:, None]
         if spec.kv_dtype == KV_F32:
             rows[start:start + n] = x
         elif spec.kv_dtype == KV_BF16:
             rows[start:start + n] = f32_to_bf16_bits(x)
         else:
-            c, s = f32_rows_to_fp8(x)
-            rows[start:start + n] = c
-            scales[start:start + n] = s
+            c8, sc = f32_rows_to_fp8(x)
+            rows[start:start + n] = c8
+            scales[start:start + n] = sc
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, tasks))
 
     # residency and pool placement
     ps = spec.page_size

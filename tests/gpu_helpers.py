@@ -1,0 +1,151 @@
+"""Shared driver for the GPU parity tests (imported by tests/test_gpu_*.py).
+
+Runs decode steps of a synthetic workload through the C ABI (select_topk ->
+resolve_rows -> sparse_mla_decode) and compares every step with the CPU
+oracle on the same seeded inputs:
+  * top-K indices, plan, counts, slot tags / stamps / reverse map / LRU
+    order and step counters: bit-exact;
+  * the pool row behind every plan entry: byte-identical to the logical row
+    (and its fp8 scale);
+  * attention: max over query rows of max_d |o - o_ref| / max_d |o_ref|
+    <= 2e-3 against the fp64 oracle (the bar the task states for bf16/fp8),
+    lse within 1e-4 relative.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from oracle import DecodeOracle, bf16_decode, mla_attention
+from sparse_mla_decode_indexer_amd import harness as Hn
+from sparse_mla_decode_indexer_amd import workload as W
+
+ATTN_TOL = 2e-3
+LSE_TOL = 1e-4
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def make_oracle(wl: W.Workload) -> DecodeOracle:
+    s = wl.spec
+    return DecodeOracle(rows=wl.rows, scales=wl.scales, kv_dtype=s.kv_dtype, host_base=wl.host_base,
+                        gpu_page=wl.gpu_page, hot_pages=wl.hot_pages, page_size=s.page_size,
+                        top_k=s.top_k, hot_rows=s.hot_rows, ctx_capacity=wl.ctx_final,
+                        sm_scale=wl.sm_scale)
+
+
+def q_f64(q: np.ndarray) -> np.ndarray:
+    return bf16_decode(q) if q.dtype == np.uint16 else q.astype(np.float64)
+
+
+def attn_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """max over query rows of max_d |o - ref| / max_d |ref| (last axis = d)."""
+    num = np.abs(out - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return float(np.max(num / np.maximum(den, 1e-30)))
+
+
+class Runner:
+    """One workload on one pool, stepped in lockstep with the oracle."""
+
+    def __init__(self, wl: W.Workload, check_state: bool = True):
+        self.wl = wl
+        self.spec = wl.spec
+        self.pool = Hn.make_pool(wl)
+        Hn.load_workload(self.pool, wl)
+        self.buf = Hn.StepBuffers(wl)
+        self.oracle = make_oracle(wl)
+        self.scores = W.ScoreStream(wl)
+        self.queries = W.QueryStream(wl)
+        self.sched = W.context_schedule(self.spec, wl.ctx0, self.spec.steps)
+        self.check_state = check_state
+        self.n = 0
+        self.raw = Hn.store_bytes(wl)
+        self.max_err = 0.0
+
+    def step(self, heads: Optional[Sequence[int]] = None, graph: bool = False):
+        """Run one step on GPU and oracle and compare. `heads` restricts the
+        attention comparison to those head indices (all query tokens)."""
+        s, wl = self.spec, self.wl
+        lens = self.sched[self.n]
+        if s.growth is not None:
+            for r in range(s.n_req):
+                Hn.set_request(self.pool, wl, r, int(lens[r]))
+        sc = self.scores.next(lens)
+        q = self.queries.next()
+        self.buf.upload(0, sc, q)
+        Hn.decode_step(self.pool, self.buf)
+        torch.cuda.synchronize()
+        ref = self.oracle.step(sc, None, lens, with_attention=False)
+        self.n += 1
+        idx = self.buf.idx.cpu().numpy()
+        plan = self.buf.plan.cpu().numpy()
+        counts = self.buf.counts.cpu().numpy()
+        tag = f"{s.name} step {self.n}"
+        for r in range(s.n_req):
+            assert np.array_equal(idx[r], ref["idx"][r]), f"{tag} req {r}: top-K differs"
+            assert np.array_equal(counts[r], ref["counts"][r]), f"{tag} req {r}: counts {counts[r]} vs {ref['counts'][r]}"
+            assert np.array_equal(plan[r], ref["plan"][r]), f"{tag} req {r}: plan differs"
+            assert counts[r].sum() == min(s.top_k, int(lens[r]))
+        if self.check_state:
+            self._check_state(tag)
+        self._check_rows(idx, plan, tag)
+        out = self.buf.out.cpu().numpy()
+        lse = self.buf.lse.cpu().numpy()
+        qd = q_f64(q)
+        for r in range(s.n_req):
+            toks = ref["idx"][r][ref["idx"][r] >= 0]
+            rows = self.oracle.logical_rows(r, toks)
+            hs = range(s.heads) if heads is None else heads
+            qr = qd[r][:, list(hs)].reshape(-1, W.ROW_DIM)
+            o_ref, l_ref = mla_attention(qr, rows, float(wl.sm_scale))
+            o = out[r][:, list(hs)].reshape(-1, W.NOPE_DIM)
+            l = lse[r][:, list(hs)].reshape(-1)
+            if rows.shape[0] == 0:
+                assert (o == 0).all() and np.isneginf(l).all(), tag
+                continue
+            e = attn_rel_err(o, o_ref)
+            self.max_err = max(self.max_err, e)
+            assert e <= ATTN_TOL, f"{tag} req {r}: attention rel err {e:.3e}"
+            le = float(np.max(np.abs(l - l_ref) / np.maximum(1.0, np.abs(l_ref))))
+            assert le <= LSE_TOL, f"{tag} req {r}: lse err {le:.3e}"
+        code = self.pool.device_error()
+        assert code[0] == 0, f"{tag}: device error {code}"
+        return ref
+
+    def _check_state(self, tag: str):
+        st = {k: v.cpu().numpy() for k, v in self.pool.state_views().items()}
+        for r in range(self.spec.n_req):
+            hb = self.oracle.hot[r]
+            assert np.array_equal(st["slot_tag"][r], hb.tag), f"{tag} req {r}: slot tags"
+            assert np.array_equal(st["slot_stamp"][r], hb.stamp), f"{tag} req {r}: stamps"
+            cap = int(self.wl.ctx_final[r])
+            assert np.array_equal(st["rev"][r][:cap], hb.rev[:cap]), f"{tag} req {r}: reverse map"
+            slots = np.arange(hb.S)
+            assert np.array_equal(st["lru_order"][r], np.lexsort((slots, hb.stamp))), f"{tag} req {r}: LRU order"
+            assert st["step"][r] == hb.step
+
+    def _check_rows(self, idx, plan, tag: str):
+        prv = self.pool.pool_row_view()
+        for r in range(self.spec.n_req):
+            ok = plan[r] >= 0
+            got = prv[torch.from_numpy(plan[r][ok].astype(np.int64)).to(prv.device)].cpu().numpy()
+            want = self.raw[self.wl.host_base[r] + idx[r][ok]]
+            assert np.array_equal(got, want), f"{tag} req {r}: pool rows differ from logical rows"
+            if self.pool.pool_scales is not None:
+                gs = self.pool.pool_scales[torch.from_numpy(plan[r][ok].astype(np.int64)).to(prv.device)].cpu().numpy()
+                assert np.array_equal(gs, self.wl.scales[self.wl.host_base[r] + idx[r][ok]]), f"{tag}: scales"
+
+    def close(self):
+        self.pool.close()
+
+
+def small(name: str, **kw) -> W.WorkloadSpec:
+    return dataclasses.replace(W.SPECS[name], **kw)

@@ -1,0 +1,70 @@
+"""The C ABI library loads without a GPU and exports what the header
+declares; host-side validation paths (no device work) behave as documented."""
+import ctypes
+import os
+
+import pytest
+
+from sparse_mla_decode_indexer_amd import binding as B
+
+
+def _lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail(f"{B.LIB_PATH} not built (run python -m sparse_mla_decode_indexer_amd.build)")
+    return B.lib()
+
+
+def test_exports_every_declared_function():
+    L = _lib()
+    names = B.header_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(B._SIGS) == set(names)
+
+
+def desc(**kw):
+    d = dict(page_size=64, num_pool_pages=128, max_requests=2, max_context=8192, nope_dim=512,
+             rope_dim=64, kv_dtype=B.HS_BF16, top_k=2048, hot_rows=0, max_batch=2, max_q_rows=128,
+             reserved0=0, host_rows=16384)
+    d.update(kw)
+    return B.HsPoolDesc(**d)
+
+
+def test_requirements_sizes():
+    _lib()
+    s = B.pool_requirements(desc())
+    assert s.row_bytes == 1152 and s.hot_rows == 4096 and s.pages_per_request == 128
+    assert s.pool_bytes == 128 * 64 * 1152 and s.pool_scale_bytes == 0
+    assert s.host_store_bytes == 16384 * 1152
+    f8 = B.pool_requirements(desc(kv_dtype=B.HS_FP8_E4M3))
+    assert f8.row_bytes == 576 and f8.pool_scale_bytes == 4 * 128 * 64
+    assert f8.host_store_bytes == 16384 * 580
+    assert B.pool_requirements(desc(kv_dtype=B.HS_F32)).row_bytes == 2304
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hot_rows=1024), 2),          # S < K
+    (dict(hot_rows=4100), 1),          # not a page multiple
+    (dict(page_size=48), 1),           # not a power of two
+    (dict(nope_dim=256), 3),
+    (dict(kv_dtype=7), 3),
+    (dict(top_k=0), 1),
+    (dict(max_batch=3), 1),
+    (dict(reserved0=1), 1),
+])
+def test_requirements_rejects(kw, status):
+    _lib()
+    with pytest.raises(B.HiSparseError) as e:
+        B.pool_requirements(desc(**kw))
+    assert e.value.status == status
+
+
+def test_null_handles_rejected_without_device_work():
+    L = _lib()
+    assert L.hs_select_topk(None, None, 0, None, 1, None, None) == 1
+    assert L.hs_resolve_rows(None, None, None, 1, None, None, None) == 1
+    assert L.hs_sparse_mla_decode(None, None, 1, 1, 1, 1, None, 0.1, None, None, None) == 1
+    assert L.hs_set_residency(None, 0, 0, 0, 0, 0, None, None, 0, None) == 1
+    assert L.hs_destroy_pool(None) == 0
+    assert B.status_string(2) == "exceeds pool capacity"

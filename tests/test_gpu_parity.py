@@ -1,0 +1,235 @@
+"""GPU parity of the decode step against the CPU oracle (through the C ABI).
+
+Reduced variants of every workload (same dtypes, heads, top-K, hot rows,
+residency rule and score process; shorter contexts) step in lockstep with
+the oracle; see gpu_helpers.Runner for what is compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Runner, log, small
+from oracle import select_topk
+from sparse_mla_decode_indexer_amd import workload as W
+from sparse_mla_decode_indexer_amd.pool import TieredPool
+
+pytestmark = pytest.mark.gpu
+
+
+def run_steps(spec, steps, heads=None):
+    log(f"[gpu] {spec.name}: ctx={spec.ctx or spec.ctx_range or spec.growth} steps={steps}")
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        for _ in range(steps):
+            rn.step(heads=heads)
+        log(f"[gpu] {spec.name}: max attention rel err {rn.max_err:.2e}")
+        return rn.max_err
+    finally:
+        rn.close()
+
+
+def test_tiny_fp32_all_steps():
+    run_steps(W.SPECS["tiny"], 8)
+
+
+def test_single_bf16_reduced():
+    run_steps(small("single-128k", ctx=16384, host_pages=192), 6)
+
+
+def test_batch_ragged_bf16_reduced():
+    # contexts 1000..20000: several requests have L < K = 2048 (all selected,
+    # -1 padding) and one has a partial last page
+    run_steps(small("batch32", n_req=6, ctx_range=(1000, 20000)), 5)
+
+
+def test_single_fp8_reduced_with_topic_shifts():
+    run_steps(small("single-1m-fp8", ctx=40000, host_pages=563, scores=("ar1_shift", 0.95, 0.5)), 6)
+
+
+def test_agent_q4_fp8_growing():
+    spec = small("agent16", n_req=3, growth=(5000, 300, 40, 2), gpu_token_budget=1 << 20)
+    run_steps(spec, 12)
+
+
+def test_small_page_and_min_hot_buffer():
+    # page size 16, S == K: every miss must reuse an untouched slot
+    spec = small("single-128k", ctx=6000, host_pages=280, page_size=16, top_k=256, hot_rows=256)
+    run_steps(spec, 6)
+
+
+@pytest.mark.parametrize("K", [1, 7, 256, 2048])
+def test_topk_ties_and_sizes(K):
+    rng = np.random.default_rng(K)
+    max_ctx = 70000
+    pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=8, max_context=max_ctx,
+                      kv_dtype="bf16", top_k=K, hot_rows=max(2 * K, 64), max_batch=8, max_q_rows=16,
+                      host_rows=8 * max_ctx)
+    try:
+        lens = [0, 1, K, K + 1, 5000, 2049, 65537, max_ctx]
+        stride = 70016
+        sc = np.zeros((8, stride), dtype=np.float32)
+        sc[0] = rng.standard_normal(stride)
+        sc[1] = -0.0
+        sc[2] = rng.integers(-2, 3, stride)
+        sc[3] = 1.0                                          # all equal
+        sc[4] = rng.integers(-3, 3, stride) * np.float32(0.5)
+        sc[4, ::3] = -0.0
+        sc[5] = rng.standard_normal(stride) * 1e-30          # tiny magnitudes
+        sc[6] = rng.standard_normal(stride).astype(np.float32)
+        sc[6, 100:200] = 1e38
+        sc[7] = rng.standard_normal(stride)
+        sc[7, rng.integers(0, max_ctx, 3000)] = 7.25          # many ties at the top
+        for r, L in enumerate(lens):
+            pool.set_residency(r, L, r * max_ctx, None)
+        d_sc = torch.from_numpy(sc).cuda()
+        req = torch.arange(8, dtype=torch.int32, device="cuda")
+        idx = torch.full((8, K), -5, dtype=torch.int32, device="cuda")
+        for rep in range(2):  # the scratch must be clean for a second call
+            pool.select_topk(d_sc, req, idx)
+            got = idx.cpu().numpy()
+            for r, L in enumerate(lens):
+                want = select_topk(sc[r], L, K)
+                assert np.array_equal(got[r], want), f"K={K} req {r} L={L} rep {rep}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
+def test_fp8_codes_exhaustive_single_row():
+    """With K = 1 the output is the selected row's value part exactly, so
+    every finite e4m3 code, widened by the kernel and scaled, must equal the
+    OCP decoding times the row scale."""
+    from oracle import e4m3fn_decode
+    spec = small("single-1m-fp8", ctx=256, host_pages=0, top_k=1, hot_rows=64, heads=16, steps=1)
+    wl = W.generate(spec)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    for t in range(wl.rows.shape[0]):
+        wl.rows[t] = np.resize(np.roll(codes, t), 576)
+    wl.scales[:] = np.float32(0.375)
+    rn = Runner(wl)
+    try:
+        rn.step()
+        out = rn.buf.out.cpu().numpy()[0, 0]
+        t = int(rn.buf.idx.cpu().numpy()[0, 0])
+        want = e4m3fn_decode(wl.rows[t][:512]) * 0.375
+        assert np.array_equal(out, np.broadcast_to(want, out.shape).astype(np.float32))
+    finally:
+        rn.close()
+
+
+def test_residency_invariance_bitwise():
+    """The same logical inputs under all-resident, 75%-host and all-host
+    layouts give bit-identical attention outputs (rows from every tier are
+    the same bytes)."""
+    outs = []
+    for hp in (0, 96, 128):
+        spec = small("single-128k", ctx=8192, host_pages=hp)
+        wl = W.generate(spec)
+        rn = Runner(wl)
+        try:
+            per = []
+            for _ in range(3):
+                rn.step(heads=range(8))
+                per.append((rn.buf.out.cpu().numpy().copy(), rn.buf.lse.cpu().numpy().copy()))
+            outs.append(per)
+        finally:
+            rn.close()
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    for a, b in zip(outs[0], outs[2]):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_unselected_rows_never_read():
+    """Poison every row that no step selects (host store and pool) with NaN
+    patterns: outputs stay finite and bit-identical to a clean run."""
+    spec = small("single-128k", ctx=8192, host_pages=96)
+    steps = 4
+    clean = W.generate(spec)
+    # selections of the run, from the oracle
+    from gpu_helpers import make_oracle
+    orc = make_oracle(clean)
+    ss = W.ScoreStream(clean)
+    used = set()
+    for _ in range(steps):
+        res = orc.step(ss.next(clean.ctx0), None, clean.ctx0, with_attention=False)
+        used.update(int(t) for t in res["idx"][0] if t >= 0)
+    runs = []
+    for poison in (False, True):
+        wl = W.generate(spec)
+        if poison:
+            mask = np.ones(wl.rows.shape[0], bool)
+            mask[list(used)] = False
+            wl.rows[mask] = 0xFFFF
+        rn = Runner(wl)
+        try:
+            outs = []
+            for _ in range(steps):
+                rn.step(heads=range(4))
+                o = rn.buf.out.cpu().numpy().copy()
+                assert np.isfinite(o).all()
+                outs.append(o)
+            runs.append(outs)
+        finally:
+            rn.close()
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+
+
+def test_graph_replay_matches_eager():
+    """The three calls captured in a hipGraph and replayed give bit-identical
+    results to eager launches, step after step (device state advances
+    without host input)."""
+    from sparse_mla_decode_indexer_amd import harness as Hn
+    spec = small("single-128k", ctx=16384, host_pages=192)
+    steps = 5
+    wl_a, wl_b = W.generate(spec), W.generate(spec)
+    pa, pb = Hn.make_pool(wl_a), Hn.make_pool(wl_b)
+    try:
+        Hn.load_workload(pa, wl_a)
+        Hn.load_workload(pb, wl_b)
+        ba, bb = Hn.StepBuffers(wl_a, n_steps=steps), Hn.StepBuffers(wl_b, n_steps=steps)
+        ss, qs = W.ScoreStream(wl_a), W.QueryStream(wl_a)
+        for n in range(steps):
+            sc, q = ss.next(wl_a.ctx0), qs.next()
+            ba.upload(n, sc, q)
+            bb.upload(n, sc, q)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        outs_b = []
+        with torch.cuda.graph(g):
+            for n in range(steps):
+                Hn.decode_step(pb, bb, n)
+                outs_b.append((bb.idx.clone(), bb.plan.clone(), bb.out.clone(), bb.lse.clone()))
+        g.replay()
+        torch.cuda.synchronize()
+        for n in range(steps):
+            Hn.decode_step(pa, ba, n)
+            torch.cuda.synchronize()
+            for x, y in zip((ba.idx, ba.plan, ba.out, ba.lse), outs_b[n]):
+                assert torch.equal(x, y), f"step {n}"
+        sa, sb = pa.state_views(), pb.state_views()
+        for k in ("slot_tag", "slot_stamp", "lru_order", "rev", "step"):
+            assert torch.equal(sa[k], sb[k]), k
+    finally:
+        pa.close()
+        pb.close()
+
+
+def test_device_error_on_index_past_context():
+    spec = small("single-128k", ctx=4096, host_pages=48, top_k=256, hot_rows=512)
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        idx = torch.arange(256, dtype=torch.int32, device="cuda")[None].clone()
+        idx[0, 5] = 5000  # past L = 4096
+        rn.pool.resolve_rows(idx, rn.buf.req_ids, rn.buf.plan, rn.buf.counts)
+        code = rn.pool.device_error()
+        assert code[0] == 1 and code[2] == 5000
+        assert rn.buf.plan[0, 5].item() == -1
+        assert rn.buf.counts[0].sum().item() == 255
+        rn.pool.clear_device_error()
+        assert rn.pool.device_error()[0] == 0
+    finally:
+        rn.close()
