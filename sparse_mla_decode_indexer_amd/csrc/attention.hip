@@ -8,20 +8,31 @@
 // For query row (request i, query token, head) -> q (576 dims):
 //   out = sum_j softmax_j(sm_scale * <q, row_j>) * row_j[0:512]
 //
-// k_attn_mfma (bf16 or fp8 rows, bf16 queries). A workgroup of 4 waves
-// takes 64 query rows of one request and a contiguous split of its plan.
-// Rows are gathered 32 at a time into LDS (fp8 codes are widened to bf16 on
-// the way, which is exact); all four waves read the staged tile, each for
-// its own 16 query rows, so each row is fetched once per workgroup.
-//   S^T (32 rows x 16 q) = K_tile (32 x 576) . Q^T     16x16x32 bf16 MFMA
-//   O^T (512 x 16 q)    += V^T (512 x 32) . P^T        16x16x32 bf16 MFMA
-// Q^T stays in registers for the whole split. The scores land with each lane
-// holding 8 rows of one query row, which is exactly the B operand layout of
-// P^T, so P never leaves registers; V^T operands come from 8x8 register
-// transposes of row-major LDS reads. P is split as p = hi + lo, two bf16
-// terms (two MFMAs), keeping ~16 significant bits of each probability; a
-// single bf16 P would cost up to 2^-8 relative error per weight. For fp8
-// rows the per-row scale multiplies the logit and p in fp32.
+// k_attn_mfma (bf16 or fp8 rows, bf16 queries). A workgroup of 8 waves
+// takes 64 query rows (4 blocks of 16) of one request and a contiguous
+// split of its plan, 32 rows (a tile) at a time:
+//   - rows are fetched straight from the pool into LDS (global_load_lds,
+//     no registers), double-buffered: tile t+1 is in flight while tile t is
+//     computed; fp8 codes land raw and are widened to bf16 in LDS (exact);
+//     absent rows read a zero row; rows sit 73 chunks of 16 bytes apart in
+//     LDS (one pad chunk), so the MFMA operand reads of 16 rows at one
+//     column hit distinct banks and operand addresses are a base plus an
+//     immediate offset;
+//   - wave (q block, half) computes the partial scores of its 16 queries over
+//     all 32 rows of the tile and its half (288) of the key dims,
+//     S^T (32 x 16 q) += K (32 x 288) . Q^T, with 16x16x32 bf16 MFMAs (its
+//     half of Q^T stays in registers); the two halves meet in LDS, so both
+//     waves of a q block then hold the full scores;
+//   - the scores land with each lane holding 8 rows of one query, exactly
+//     the B operand of P^T: p stays in registers, split as hi + lo bf16
+//     terms (~16 significant bits per weight; a single bf16 term would cost
+//     up to 2^-8 relative error per weight); fp8 rows fold their scale into
+//     the logit and into p in fp32;
+//   - PV: O^T (256 dims x 16 q) += V^T . P^T; V^T operands come from 8x8
+//     register transposes of row-major LDS reads, in the same row order as
+//     P^T;
+//   - two workgroup barriers per tile: tile landed / previous tile retired,
+//     and the partial-score exchange.
 // Softmax is online (running max and sum in fp32, base 2). With more than
 // one split, each split writes a normalised partial output and its
 // log-sum-exp; k_attn_combine merges them.
@@ -40,12 +51,17 @@ namespace hs {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kAttThreads = 256;       // 4 waves
-constexpr int kQPerWave = 16;
-constexpr int kQPerWG = 64;
-constexpr int kTile = 32;              // rows per staged tile
-constexpr int kLdsRow = 2 * kRowDim + 16;  // bf16 row + 16 bytes of padding
+constexpr int kAttThreads = 512;       // 8 waves
+constexpr int kQPerWG = 64;            // 4 blocks of 16 query rows
+constexpr int kTile = 32;              // rows per tile
+constexpr int kChunks = 2 * kRowDim / 16;        // 72 chunks of 16 B per bf16 row
+constexpr int kRowChunks = kChunks + 1;          // LDS row stride: 73 chunks (one pad chunk)
+constexpr int kTilePos = kTile * kRowChunks;     // 2336 chunk positions per tile
+constexpr int kTileBytes = kTilePos * 16;        // 37376
+constexpr int kRawChunks = kRowDim / 16;         // 36 chunks per fp8 row
+constexpr int kRawTileBytes = kTile * kRawChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -70,181 +86,256 @@ __device__ inline void fp8x4_to_bf16(uint32_t w, uint32_t* o) {
   o[1] = pack_hi(f23[0], f23[1]);
 }
 
-// Row of the tile held in position e (0..7) of a lane's P^T / V^T k-vector:
-// the scores of rows 4*kg + 0..3 and 16 + 4*kg + 0..3 land in lane group kg.
+// Workgroup barrier for LDS exchanges that leaves the tile prefetch in
+// flight: wait for this wave's own LDS accesses (lgkmcnt 0 only), then
+// s_barrier, with compiler-level memory barriers on both sides. A release
+// fence (as in __syncthreads) would also wait for the global->LDS DMA of the
+// next tile, since that DMA is an LDS write of this wave.
+__device__ inline void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Row of the tile in position e (0..7) of a lane's k-vector: the scores of
+// rows 4*kg + 0..3 and 16 + 4*kg + 0..3 land in lane group kg = lane / 16.
 __device__ inline int krow(int kg, int e) { return (e < 4) ? 4 * kg + e : 16 + 4 * kg + (e - 4); }
+
+// Reductions over the 4 lanes l, l^16, l^32, l^48 that hold one query:
+// each swap returns {x[l], x[l^32]} (or l^16) as a pair, in some order.
+__device__ inline float max_across_kg(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_across_kg(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS chunk position of 16-byte chunk c of tile row r.
+__device__ inline int swz(int r, int c) { return r * kRowChunks + c; }
 
 template <bool FP8>
 __global__ __launch_bounds__(kAttThreads) void k_attn_mfma(
     const uint16_t* __restrict__ q, int QR, const int32_t* __restrict__ plan, int K,
     const uint8_t* __restrict__ pool, const float* __restrict__ pool_scales, int64_t pool_rows_n,
-    float c2, int tiles_per_split, int n_splits, float* __restrict__ out, float* __restrict__ lse_out,
-    float* __restrict__ part_o, float* __restrict__ part_lse, uint32_t* __restrict__ err) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kLdsRow];
-  __shared__ float kvs[kTile];
-  __shared__ int prow_s[kTile];
+    const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
+    float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o,
+    float* __restrict__ part_lse, uint32_t* __restrict__ err) {
+  // Two distinct LDS buffers (not one indexed array) so that the compiler
+  // can tell the DMA into one from the reads of the other and does not wait
+  // for the prefetch before computing.
+  __shared__ __attribute__((aligned(16))) uint8_t bufA[FP8 ? kRawTileBytes : kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t bufB[FP8 ? kRawTileBytes : kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wide[FP8 ? kTileBytes : 16];
+  __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
+  __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
+  __shared__ f32x4_t sbuf[2][4][2][64];  // partial scores [key half][q block][row block][lane]
 
   const int sp = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, ln = lane & 15;
-  const int qh = hg * kQPerWG + wave * kQPerWave + ln;
+  const int qb = wave & 3, half = wave >> 2;  // query block; key-dim half (QK) and value-dim half (PV)
+  const int qh = hg * kQPerWG + qb * 16 + ln;
   const bool qvalid = qh < QR;
   const int32_t* pl = plan + (size_t)i * K;
+  const int n_tiles = (K + kTile - 1) / kTile;
+  const int t_begin = sp * tiles_per_split;
+  const int nt = min(n_tiles, t_begin + tiles_per_split) - t_begin;
 
-  // Q^T operand: lane holds query row qh, dims 32*kk + 8*kg .. +8
-  u32x4_t qop[kRowDim / 32];
+  // plan rows (and fp8 scales) of this split
+  for (int j = tid; j < nt * kTile; j += kAttThreads) {
+    const int jj = t_begin * kTile + j;
+    int pr = jj < K ? pl[jj] : -1;
+    if (pr >= pool_rows_n) {
+      raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)jj);
+      pr = -1;
+    }
+    prow_s[j] = pr;
+    if (FP8) scale_s[j] = pr >= 0 ? pool_scales[pr] : 0.f;
+  }
+  // Q^T operand for key dims 288*half .. +288: lane holds query row qh,
+  // dims 288*half + 32*kk + 8*kg .. +8
+  constexpr int kKSteps = kRowDim / 64;  // 9
+  u32x4_t qop[kKSteps];
   {
-    const uint16_t* qr = q + ((size_t)i * QR + (qvalid ? qh : 0)) * kRowDim;
+    const uint16_t* qr = q + ((size_t)i * QR + (qvalid ? qh : 0)) * kRowDim + 288 * half;
 #pragma unroll
-    for (int kk = 0; kk < kRowDim / 32; ++kk) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * kg);
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * kg);
       qop[kk] = qvalid ? x : u32x4_t{0, 0, 0, 0};
     }
   }
-  f32x4_t acc[4][8];
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();
 
-  const int n_tiles = (K + kTile - 1) / kTile;
-  const int t_begin = sp * tiles_per_split;
-  const int t_end = min(n_tiles, t_begin + tiles_per_split);
-  for (int tt = t_begin; tt < t_end; ++tt) {
-    if (tid < kTile) {
-      const int j = tt * kTile + tid;
-      int pr = j < K ? pl[j] : -1;
-      if (pr >= pool_rows_n) {
-        raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)j);
-        pr = -1;
-      }
-      prow_s[tid] = pr;
-      kvs[tid] = FP8 ? (pr >= 0 ? pool_scales[pr] : 0.f) : 1.f;
-    }
-    __syncthreads();
+  // Start the gather of tile t into `dst` (wave-contiguous LDS targets).
+  auto issue = [&](int t, uint8_t* dst) {
     if (!FP8) {
-      constexpr int CH = 2 * kRowDim / 16;  // 72 chunks of 16 B per row
-      for (int c = tid; c < kTile * CH; c += kAttThreads) {
-        const int r = c / CH, ch = c - r * CH;
-        const int pr = prow_s[r];
-        u32x4_t x = u32x4_t{0, 0, 0, 0};
-        if (pr >= 0) x = *reinterpret_cast<const u32x4_t*>(pool + (size_t)pr * (2 * kRowDim) + ch * 16);
-        *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + ch * 16) = x;
+#pragma unroll
+      for (int k = 0; k < (kTilePos + kAttThreads - 1) / kAttThreads; ++k) {
+        const int p = k * kAttThreads + tid;
+        if (k * kAttThreads + wave * 64 < kTilePos) {  // wave-uniform
+          const int r = p / kRowChunks, c = p - r * kRowChunks;
+          if (p < kTilePos && c < kChunks) {  // pad chunks are never read
+            const int pr = prow_s[t * kTile + r];
+            const uint8_t* src = pr >= 0 ? pool + (size_t)pr * (2 * kRowDim) + c * 16 : zero_row + c * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16),
+                                             16, 0, 0);
+          }
+        }
       }
     } else {
-      constexpr int CH = kRowDim / 16;  // 36 chunks of 16 codes per row
-      for (int c = tid; c < kTile * CH; c += kAttThreads) {
-        const int r = c / CH, ch = c - r * CH;
-        const int pr = prow_s[r];
-        u32x4_t x = u32x4_t{0, 0, 0, 0};
-        if (pr >= 0) x = *reinterpret_cast<const u32x4_t*>(pool + (size_t)pr * kRowDim + ch * 16);
-        uint32_t w[8];
-        fp8x4_to_bf16(x[0], w);
-        fp8x4_to_bf16(x[1], w + 2);
-        fp8x4_to_bf16(x[2], w + 4);
-        fp8x4_to_bf16(x[3], w + 6);
-        *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + ch * 32) = u32x4_t{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4_t*>(tile + r * kLdsRow + ch * 32 + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+#pragma unroll
+      for (int k = 0; k < (kTile * kRawChunks + kAttThreads - 1) / kAttThreads; ++k) {
+        const int p = k * kAttThreads + tid;
+        if (k * kAttThreads + wave * 64 < kTile * kRawChunks) {
+          const int r = p / kRawChunks, c = p - r * kRawChunks;
+          const int pr = prow_s[t * kTile + r];
+          const uint8_t* src = pr >= 0 ? pool + (size_t)pr * kRowDim + c * 16 : zero_row + c * 16;
+          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16),
+                                           16, 0, 0);
+        }
       }
     }
-    __syncthreads();
+  };
 
-    // S^T = K_tile . Q^T, two 16-row blocks
+  f32x4_t acc[2][8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, lpart = 0.f;
+
+  // One tile: wait for it, start the next gather into `nxt`, compute on `cur`.
+  auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t has landed
+    lds_sync();                      // all of tile t is in LDS; tile t-1 is done
+    if (t + 1 < nt) issue(t + 1, nxt);
+    const uint8_t* T = FP8 ? wide : cur;
+    if (FP8) {  // widen the raw codes of tile t into the bf16 tile
+      for (int x = tid; x < kTile * kRawChunks; x += kAttThreads) {
+        const int r = x / kRawChunks, c = x - r * kRawChunks;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cur + x * 16);
+        uint32_t w[8];
+        fp8x4_to_bf16(v[0], w);
+        fp8x4_to_bf16(v[1], w + 2);
+        fp8x4_to_bf16(v[2], w + 4);
+        fp8x4_to_bf16(v[3], w + 6);
+        *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c + 1) * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+      }
+      lds_sync();
+    }
+    // QK partial over key dims 288*half .. +288, all 32 rows of the tile
     f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int kk = 0; kk < kRowDim / 32; ++kk) {
+    for (int kk = 0; kk < kKSteps; ++kk) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(tile + (16 * rb + ln) * kLdsRow + (32 * kk + 8 * kg) * 2);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(T + swz(16 * rb + ln, 36 * half + 4 * kk + kg) * 16);
         sacc[rb] = mfma16(a, qop[kk], sacc[rb]);
       }
     }
-    // base-2 logits of this lane's 8 rows, masked rows at -inf
+    sbuf[half][qb][0][lane] = sacc[0];
+    sbuf[half][qb][1][lane] = sacc[1];
+    lds_sync();
+    sacc[0] += sbuf[half ^ 1][qb][0][lane];
+    sacc[1] += sbuf[half ^ 1][qb][1][lane];
+    // base-2 logits; lane holds rows krow(kg, e) of query ln
     float s[8], rs[8];
+    float pm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int row = krow(kg, e);
-      rs[e] = kvs[row];
+      const int row = t * kTile + krow(kg, e);
+      rs[e] = FP8 ? scale_s[row] : 1.f;
       const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
       s[e] = prow_s[row] >= 0 ? raw * (c2 * rs[e]) : -INFINITY;
+      pm = fmaxf(pm, s[e]);
     }
-    float tmax = s[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
+    pm = max_across_kg(pm);
+    const float m_new = fmaxf(m_run, pm);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);
-      psum += p[e];
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
     m_run = m_new;
+    u32x4_t bhi, blo;  // P^T operand (hi and lo parts), rows krow(kg, 0..7)
+    {
+      float psum = 0.f, a[8], lo[8];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(s[e] - m_use);
+        psum += pe;
+        a[e] = FP8 ? pe * rs[e] : pe;
+        lo[e] = a[e] - __uint_as_float(__float_as_uint(a[e]) & 0xFFFF0000u);
+      }
+      lpart = lpart * alpha + psum;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
-    // P^T operand as hi + lo bf16 parts; fp8 rows carry their scale in p
-    u32x4_t phi, plo;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float a = FP8 ? p[2 * d] * rs[2 * d] : p[2 * d];
-      const float b = FP8 ? p[2 * d + 1] * rs[2 * d + 1] : p[2 * d + 1];
-      const float ah = __uint_as_float(__float_as_uint(a) & 0xFFFF0000u);
-      const float bh = __uint_as_float(__float_as_uint(b) & 0xFFFF0000u);
-      phi[d] = pack_hi(a, b);
-      plo[d] = pack_hi(a - ah, b - bh);
+      for (int d = 0; d < 4; ++d) {
+        bhi[d] = pack_hi(a[2 * d], a[2 * d + 1]);
+        blo[d] = pack_hi(lo[2 * d], lo[2 * d + 1]);
+      }
     }
-    // O^T += V^T . P^T, four groups of 128 value dims
+
+    // PV: dims 256*half .. +256 of this wave's 16 queries
+    if (__any(alpha != 1.f)) {  // the running max moved for some query of this wave
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
       u32x4_t R[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        R[e] = *reinterpret_cast<const u32x4_t*>(tile + krow(kg, e) * kLdsRow + (128 * g + 8 * ln) * 2);
+      for (int j = 0; j < 8; ++j)
+        R[j] = *reinterpret_cast<const u32x4_t*>(T + swz(krow(kg, j), 32 * half + 16 * g + ln) * 16);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        u32x4_t A0, A1;  // dims 8*ln + 2w and 8*ln + 2w + 1
+        u32x4_t A0, A1;  // dims 8*ln + 2w and 8*ln + 2w + 1 over rows krow(kg, 0..7)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint32_t x = R[2 * d][w], y = R[2 * d + 1][w];
           A0[d] = (x & 0xFFFFu) | (y << 16);
           A1[d] = (x >> 16) | (y & 0xFFFF0000u);
         }
-        acc[g][2 * w] = mfma16(A0, phi, acc[g][2 * w]);
-        acc[g][2 * w + 1] = mfma16(A1, phi, acc[g][2 * w + 1]);
-        acc[g][2 * w] = mfma16(A0, plo, acc[g][2 * w]);
-        acc[g][2 * w + 1] = mfma16(A1, plo, acc[g][2 * w + 1]);
+        acc[g][2 * w] = mfma16(A0, bhi, acc[g][2 * w]);
+        acc[g][2 * w + 1] = mfma16(A1, bhi, acc[g][2 * w + 1]);
+        acc[g][2 * w] = mfma16(A0, blo, acc[g][2 * w]);
+        acc[g][2 * w + 1] = mfma16(A1, blo, acc[g][2 * w + 1]);
       }
     }
-    __syncthreads();
+  };
+
+  issue(0, bufA);
+  for (int t = 0; t < nt; t += 2) {
+    tile(t, bufA, bufB);
+    if (t + 1 < nt) tile(t + 1, bufB, bufA);
   }
 
+  // softmax denominator: sum over the 4 lanes (row groups) of each query
+  const float l = sum_across_kg(lpart);
   if (!qvalid) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse2 = l > 0.f ? m_run + __log2f(l) : -INFINITY;
   float* dst;
   if (n_splits == 1) {
     dst = out + ((size_t)i * QR + qh) * kNope;
-    if (lse_out && kg == 0) lse_out[(size_t)i * QR + qh] = lse2 * kLn2;
+    if (lse_out && kg == 0 && half == 0) lse_out[(size_t)i * QR + qh] = lse2 * kLn2;
   } else {
     const size_t prow = ((size_t)i * n_splits + sp) * QR + qh;
     dst = part_o + prow * kNope;
-    if (kg == 0) part_lse[prow] = lse2;
+    if (kg == 0 && half == 0) part_lse[prow] = lse2;
   }
-  // lane holds dims 128g + 32kg + 8v + c, c = 0..7, for v = 0..3
+  // lane holds dims 256*half + 128g + 32kg + 8v + c, c = 0..7, v = 0..3
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float* o = dst + 128 * g + 32 * kg + 8 * v;
+      float* o = dst + 256 * half + 128 * g + 32 * kg + 8 * v;
       *reinterpret_cast<float4*>(o) = make_float4(acc[g][0][v] * inv, acc[g][1][v] * inv,
                                                   acc[g][2][v] * inv, acc[g][3][v] * inv);
       *reinterpret_cast<float4*>(o + 4) = make_float4(acc[g][4][v] * inv, acc[g][5][v] * inv,
@@ -366,24 +457,30 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   }
   const int n_tiles = (K + kTile - 1) / kTile;
   const int n_hg = (QR + kQPerWG - 1) / kQPerWG;
+  const uint8_t* zero_row = p->state + p->off.zero_row;
   // Split the plan so that the grid covers the chip; a split is at least
   // two tiles so that a workgroup's partial output stays below its row bytes.
+  // Split the plan so that about one workgroup per CU is busy; a split is at
+  // least 4 tiles so that the fixed cost per workgroup (plan, queries,
+  // partial output) is amortised.
   static const int forced = env_int("HS_ATTN_TILES_PER_SPLIT", 0);
   int tps;
   if (forced > 0) {
     tps = forced;
   } else {
     const int base = n_req * n_hg;
-    int splits = (512 + base - 1) / base;
-    tps = (n_tiles + splits - 1) / splits;
-    if (tps < 2) tps = 2;
+    const int want = (256 + base - 1) / base;
+    tps = (n_tiles + want - 1) / want;
+    if (tps < 4) tps = 4;
   }
   if (tps > n_tiles) tps = n_tiles;
+  if (tps > kAttMaxTilesPerSplit) tps = kAttMaxTilesPerSplit;
   int splits = (n_tiles + tps - 1) / tps;
   while (splits > 1 && (int64_t)n_req * QR * splits > p->off.at_part_rows) {
     ++tps;
     splits = (n_tiles + tps - 1) / tps;
   }
+  if (tps > kAttMaxTilesPerSplit) return HS_ERR_CAPACITY;  // cannot happen for top_k <= 4096
   float* part_o = reinterpret_cast<float*>(p->state + p->off.at_part_o);
   float* part_lse = reinterpret_cast<float*>(p->state + p->off.at_part_lse);
   const float c2 = sm_scale * kLog2e;
@@ -391,11 +488,12 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   if (p->d.kv_dtype == HS_BF16)
     k_attn_mfma<false><<<grid, kAttThreads, 0, s>>>(q16, QR, plan, K, p->pool_rows, nullptr, p->pool_rows_n,
-                                                    c2, tps, splits, out, lse_out, part_o, part_lse, err);
+                                                    zero_row, c2, tps, splits, out, lse_out, part_o, part_lse,
+                                                    err);
   else
     k_attn_mfma<true><<<grid, kAttThreads, 0, s>>>(q16, QR, plan, K, p->pool_rows, p->pool_scales,
-                                                   p->pool_rows_n, c2, tps, splits, out, lse_out, part_o,
-                                                   part_lse, err);
+                                                   p->pool_rows_n, zero_row, c2, tps, splits, out, lse_out,
+                                                   part_o, part_lse, err);
   if (splits > 1) {
     const int rows = n_req * QR;
     k_attn_combine<<<(rows + 3) / 4, 256, 0, s>>>(rows, QR, splits, part_o, part_lse, out, lse_out);

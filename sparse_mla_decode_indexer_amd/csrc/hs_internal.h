@@ -21,6 +21,7 @@ constexpr int kTkThreads = 256;
 constexpr int kTkBins = 4096;      // 12-bit radix digits
 constexpr int kTkFinalThreads = 1024;
 constexpr int kTkMaxChunks = 2048; // => max_context <= 4,194,304
+constexpr int kTkFinalStage = 8192; // survivors staged in LDS by the final pass
 
 // resolve
 constexpr int kRsThreads = 1024;
@@ -28,9 +29,12 @@ constexpr int kCopyThreads = 256;
 
 // attention
 constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)
+constexpr int kAttMinPartRows = 16384;  // at least this many partial rows (32 MiB)
+constexpr int kAttMaxTilesPerSplit = 64;
 
 // ---------------------------------------------------------------- the handle
 struct Offsets {
+  size_t zero_row;  // kRowDim * 4 bytes of zeros, never written after init
   size_t tk_hist, tk_done, tk_sel, tk_count, tk_cand;
   size_t rs_miss_count, rs_miss_src, rs_miss_dst;
   size_t at_part_o, at_part_lse;

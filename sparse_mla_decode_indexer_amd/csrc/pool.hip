@@ -81,6 +81,7 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   L.error = take(16);
   L.scratch = o;
   Offsets of{};
+  of.zero_row = take(4 * kRowDim);
   const size_t max_chunks = ((size_t)d->max_context + kTkChunk - 1) / kTkChunk;
   of.tk_hist = take(4 * B * kTkBins);
   of.tk_done = take(4 * B);
@@ -91,6 +92,7 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   of.rs_miss_src = take(8 * B * K);
   of.rs_miss_dst = take(4 * B * K);
   of.at_part_rows = (int64_t)B * d->max_q_rows * kAttSplitCap;
+  if (of.at_part_rows < kAttMinPartRows) of.at_part_rows = kAttMinPartRows;
   of.at_part_o = take(4 * (size_t)of.at_part_rows * kNope);
   of.at_part_lse = take(4 * (size_t)of.at_part_rows);
   L.total = o;

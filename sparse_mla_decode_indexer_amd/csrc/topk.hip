@@ -14,9 +14,9 @@
 //   k_topk_filter  the same workgroups: keep every key whose top digit is
 //                  >= b1, compacted in index order into the chunk's slice of
 //                  a candidate buffer (about K + a few thousand survive).
-//   k_topk_final   one workgroup per request: two more radix passes over the
-//                  survivors give T, then an ordered compaction writes the
-//                  selected token ids.
+//   k_topk_final   one workgroup per request: the survivors are staged in LDS
+//                  (when they fit); two more radix passes over them give T,
+//                  then an ordered compaction writes the selected token ids.
 // Every kernel has a fixed grid and leaves its scratch cleared, so the
 // sequence replays under a hipGraph without host input.
 #include <hip/hip_runtime.h>
@@ -108,12 +108,18 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_hist(const float* __restric
   if (tid == 0) last = (atomicAdd(&sc.done[i], 1u) == (uint32_t)(nch - 1));
   __syncthreads();
   if (!last) return;
+  // Last workgroup of this request: the acquire fence makes every other
+  // workgroup's additions visible to plain loads. All 16 loads of a thread
+  // are issued before any is used; the totals are cleared for next time.
   __threadfence();
-  // Last workgroup of this request: every other workgroup's additions are
-  // visible. Read the totals at device scope and clear them for next time.
-  for (int b = tid; b < kTkBins; b += kTkThreads) {
-    h[b] = __hip_atomic_load(&gh[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    gh[b] = 0;
+  constexpr int PER = kTkBins / kTkThreads;
+  uint32_t cnt[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) cnt[k] = gh[k * kTkThreads + tid];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    h[k * kTkThreads + tid] = cnt[k];
+    gh[k * kTkThreads + tid] = 0;
   }
   __syncthreads();
   int b1, above;
@@ -183,9 +189,10 @@ __global__ __launch_bounds__(kTkFinalThreads) void k_topk_final(const int32_t* _
                                                                 int32_t* __restrict__ idx_out) {
   __shared__ uint32_t h[kTkBins];
   __shared__ int off[kTkMaxChunks + 1];
+  __shared__ uint2 surv[kTkFinalStage];
   __shared__ int tmp[kTkFinalThreads / 64 + 1];
   __shared__ int res[2];
-  const int i = blockIdx.x, tid = threadIdx.x;
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = v.top_k;
   int32_t* out = idx_out + (size_t)i * K;
   const int r = request_of(req_ids, i, v);
@@ -206,15 +213,27 @@ __global__ __launch_bounds__(kTkFinalThreads) void k_topk_final(const int32_t* _
     run += tot;
   }
   if (tid == 0) off[nch] = run;
+  __syncthreads();
   const int total = run;
+  const uint2* cand = sc.cand + (size_t)i * sc.max_chunks * kTkChunk;
+  // Survivors in index order: staged in LDS when they fit (one wave copies
+  // one chunk slice), otherwise read from the chunk slices in place.
+  const bool staged = total <= kTkFinalStage;
+  if (staged) {
+    for (int c = wave; c < nch; c += kTkFinalThreads / 64) {
+      const int o = off[c], n = off[c + 1] - o;
+      for (int j = lane; j < n; j += 64) surv[o + j] = cand[(size_t)c * kTkChunk + j];
+    }
+    __syncthreads();
+  }
+  auto get = [&](int x) -> uint2 { return staged ? surv[x] : survivor(cand, off, nch, x); };
   const uint32_t b1 = (uint32_t)sc.sel[4 * i];
   const int need1 = K - sc.sel[4 * i + 1];
-  const uint2* cand = sc.cand + (size_t)i * sc.max_chunks * kTkChunk;
   // pass 2: bits 19..8 of the keys whose top digit is b1
   for (int b = tid; b < kTkBins; b += kTkFinalThreads) h[b] = 0;
   __syncthreads();
   for (int x = tid; x < total; x += kTkFinalThreads) {
-    const uint2 kv = survivor(cand, off, nch, x);
+    const uint2 kv = get(x);
     if ((kv.x >> 20) == b1) atomicAdd(&h[(kv.x >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
@@ -226,7 +245,7 @@ __global__ __launch_bounds__(kTkFinalThreads) void k_topk_final(const int32_t* _
   for (int b = tid; b < kTkBins; b += kTkFinalThreads) h[b] = 0;
   __syncthreads();
   for (int x = tid; x < total; x += kTkFinalThreads) {
-    const uint2 kv = survivor(cand, off, nch, x);
+    const uint2 kv = get(x);
     if ((kv.x >> 8) == pre24) atomicAdd(&h[kv.x & 0xFFu], 1u);
   }
   __syncthreads();
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(kTkFinalThreads) void k_topk_final(const int32_t* _
   for (int base = 0; base < total; base += kTkFinalThreads) {
     const int x = base + tid;
     uint2 kv = make_uint2(0u, 0u);
-    if (x < total) kv = survivor(cand, off, nch, x);
+    if (x < total) kv = get(x);
     const bool eq = x < total && kv.x == T;
     int eq_tot;
     const int tie_rank = tie_run + block_excl_count(eq, tmp, eq_tot);

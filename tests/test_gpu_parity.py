@@ -48,7 +48,7 @@ def test_single_fp8_reduced_with_topic_shifts():
 
 
 def test_agent_q4_fp8_growing():
-    spec = small("agent16", n_req=3, growth=(5000, 300, 40, 2), gpu_token_budget=1 << 20)
+    spec = small("agent16", n_req=3, growth=(5000, 300, 40, 2), gpu_token_budget=1 << 20, steps=20)
     run_steps(spec, 12)
 
 
