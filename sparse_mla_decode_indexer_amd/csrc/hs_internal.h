@@ -15,17 +15,15 @@ constexpr int kNope = 512;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHotRows = 8192;
 
-// top-K: one workgroup scans one chunk of kTkChunk scores
+// top-K: one filter workgroup scans one chunk of kTkChunk scores
 constexpr int kTkChunk = 2048;
 constexpr int kTkThreads = 256;
 constexpr int kTkBins = 4096;      // 12-bit radix digits
-constexpr int kTkFinalThreads = 1024;
 constexpr int kTkMaxChunks = 2048; // => max_context <= 4,194,304
-constexpr int kTkFinalStage = 8192; // survivors staged in LDS by the final pass
+constexpr int kTkStage = 8192;     // survivors staged in LDS by the select workgroup
 
 // resolve
 constexpr int kRsThreads = 1024;
-constexpr int kCopyThreads = 256;
 
 // attention
 constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)
@@ -35,8 +33,8 @@ constexpr int kAttMaxTilesPerSplit = 64;
 // ---------------------------------------------------------------- the handle
 struct Offsets {
   size_t zero_row;  // kRowDim * 4 bytes of zeros, never written after init
-  size_t tk_hist, tk_done, tk_sel, tk_count, tk_cand;
-  size_t rs_miss_count, rs_miss_src, rs_miss_dst;
+  size_t tk_count, tk_max, tk_cand, tk_bound;
+  size_t rs_miss_mask, rs_flag, rs_exit, rs_ticket;
   size_t at_part_o, at_part_lse;
   int64_t at_part_rows;  // capacity of partial rows
 };

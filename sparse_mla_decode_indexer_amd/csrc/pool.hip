@@ -83,14 +83,14 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   Offsets of{};
   of.zero_row = take(4 * kRowDim);
   const size_t max_chunks = ((size_t)d->max_context + kTkChunk - 1) / kTkChunk;
-  of.tk_hist = take(4 * B * kTkBins);
-  of.tk_done = take(4 * B);
-  of.tk_sel = take(16 * B);
   of.tk_count = take(4 * B * max_chunks);
+  of.tk_max = take(4 * B * max_chunks);
   of.tk_cand = take(8 * B * max_chunks * kTkChunk);
-  of.rs_miss_count = take(4 * B);
-  of.rs_miss_src = take(8 * B * K);
-  of.rs_miss_dst = take(4 * B * K);
+  of.tk_bound = take(4 * R);
+  of.rs_miss_mask = take(8 * B * ((K + 63) / 64));
+  of.rs_flag = take(4 * B);
+  of.rs_exit = take(4 * B);
+  of.rs_ticket = take(8);
   of.at_part_rows = (int64_t)B * d->max_q_rows * kAttSplitCap;
   if (of.at_part_rows < kAttMinPartRows) of.at_part_rows = kAttMinPartRows;
   of.at_part_o = take(4 * (size_t)of.at_part_rows * kNope);

@@ -3,34 +3,45 @@
 // indexer picks). Per request: the min(K, L) largest scores, equal scores
 // keeping the lower token index, output in ascending token order.
 //
-// Scores map to order-preserving 32-bit keys (-0.0 folded onto +0.0). The
-// exact K-th largest key T is found by a radix select over 12 + 12 + 8 bits;
-// a token is selected when key > T, or key == T and it is among the first
-// (K - #{key > T}) tokens with key T in index order.
+// Scores map to order-preserving 32-bit keys (-0.0 folded onto +0.0). A
+// token is selected when key > T, or key == T and it is among the first
+// (K - #{key > T}) tokens with key T in token order, where T is the exact
+// K-th largest key.
 //
-//   k_topk_hist    many workgroups per request: histogram of the top 12 key
-//                  bits; the last workgroup to finish finds the digit b1 of
-//                  the K-th largest key and clears the histogram.
-//   k_topk_filter  the same workgroups: keep every key whose top digit is
-//                  >= b1, compacted in index order into the chunk's slice of
-//                  a candidate buffer (about K + a few thousand survive).
-//   k_topk_final   one workgroup per request: the survivors are staged in LDS
-//                  (when they fit); two more radix passes over them give T,
-//                  then an ordered compaction writes the selected token ids.
-// Every kernel has a fixed grid and leaves its scratch cleared, so the
-// sequence replays under a hipGraph without host input.
+// Two kernels per call:
+//   k_topk_filter  workgroup (c, i) reads scores [2048c, 2048c + 2048) of
+//                  request i, keeps every key >= the request's bound, in
+//                  token order, in its slice of a candidate buffer (ballot
+//                  ranks, no LDS tables, no atomics) and writes the slice's
+//                  count and largest key. Many small workgroups per CU.
+//   k_topk_select  one 1024-thread workgroup per request: stages the
+//                  survivors in LDS in token order, finds T by a radix
+//                  select over (key - bound) whose digit widths follow the
+//                  survivors' key range (usually two 12-bit digits), writes
+//                  the selected tokens in order and sets the next bound.
+// The bound carried from call to call only decides how much work is done;
+// the result is exact in every case. The next bound is the lower edge of the
+// first-digit bin holding the survivor of rank 5K/4, so that about 1.25K
+// scores pass next time when scores move little between steps; with fewer
+// than 5K/4 survivors it is lowered instead. If fewer than K scores pass (a
+// bound too high) the select runs over the raw scores; if more pass than
+// LDS holds (e.g. the first call, bound 0) it reads them from the candidate
+// buffer. Grids are fixed and no scratch needs clearing, so the pair
+// replays under a hipGraph without host input.
 #include <hip/hip_runtime.h>
 
 #include "hs_internal.h"
 
 namespace hs {
 
+constexpr int kTkSelThreads = 1024;
+constexpr int kTkSelWaves = kTkSelThreads / 64;
+
 struct TkScratch {
-  uint32_t* hist;   // [batch][kTkBins]
-  uint32_t* done;   // [batch]
-  int32_t* sel;     // [batch][4]: b1, #keys with top digit > b1
-  int32_t* count;   // [batch][max_chunks]
-  uint2* cand;      // [batch][max_chunks * kTkChunk] (key, token)
+  int32_t* count;   // [batch][max_chunks] survivors per chunk
+  uint32_t* maxk;   // [batch][max_chunks] largest surviving key per chunk
+  uint2* cand;      // [batch][max_chunks * kTkChunk] (key, token), chunk slices
+  uint32_t* bound;  // [max_requests] survivor bound for the next call
   int32_t max_chunks;
 };
 
@@ -40,234 +51,330 @@ __device__ inline uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Scan the histogram h[0..nbins) from the top bin down and find the bin b
-// with above(b) < need <= above(b) + h[b], where above(b) = sum of bins > b.
-// Every thread gets (b, above(b)). nbins must be a multiple of blockDim.x.
-__device__ inline void find_digit(const uint32_t* h, int nbins, int need, int* tmp, int* res,
-                                  int& b_out, int& above_out) {
-  const int per = nbins / blockDim.x;
-  const int hi = nbins - per * threadIdx.x;  // this thread owns bins [hi-per, hi)
-  int mine = 0;
-  for (int b = hi - 1; b >= hi - per; --b) mine += (int)h[b];
-  int tot;
-  int above = block_excl_sum(mine, tmp, tot);
-  for (int b = hi - 1; b >= hi - per; --b) {
-    const int c = (int)h[b];
-    if (above < need && above + c >= need) {
-      res[0] = b;
-      res[1] = above;
-    }
-    above += c;
-  }
-  __syncthreads();
-  b_out = res[0];
-  above_out = res[1];
-  __syncthreads();
-}
-
 __device__ inline int request_of(const int32_t* req_ids, int i, const StateView& v) {
   const int r = req_ids[i];
   return (r >= 0 && r < v.max_requests) ? r : -1;
 }
 
-__global__ __launch_bounds__(kTkThreads) void k_topk_hist(const float* __restrict__ scores,
-                                                          int64_t stride,
-                                                          const int32_t* __restrict__ req_ids,
-                                                          StateView v, TkScratch sc) {
-  __shared__ uint32_t h[kTkBins];
-  __shared__ int tmp[kTkThreads / 64 + 1];
-  __shared__ int res[2];
-  __shared__ int last;
-  const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int r = request_of(req_ids, i, v);
-  if (r < 0) {
-    if (c == 0 && tid == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, (uint32_t)req_ids[i]);
-    return;
-  }
-  const int L = v.ctx_len[r], K = v.top_k;
-  if (L <= K) return;
-  const int nch = (L + kTkChunk - 1) / kTkChunk;
-  if (c >= nch) return;
-  for (int b = tid; b < kTkBins; b += kTkThreads) h[b] = 0;
-  __syncthreads();
-  const float* s = scores + (size_t)i * stride;
-  const int base = c * kTkChunk;
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
 #pragma unroll
-  for (int e = 0; e < kTkChunk / kTkThreads; ++e) {
-    const int t = base + e * kTkThreads + tid;
-    if (t < L) atomicAdd(&h[score_key(s[t]) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = sc.hist + (size_t)i * kTkBins;
-  for (int b = tid; b < kTkBins; b += kTkThreads) {
-    const uint32_t x = h[b];
-    if (x) atomicAdd(&gh[b], x);
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(&sc.done[i], 1u) == (uint32_t)(nch - 1));
-  __syncthreads();
-  if (!last) return;
-  // Last workgroup of this request: the acquire fence makes every other
-  // workgroup's additions visible to plain loads. All 16 loads of a thread
-  // are issued before any is used; the totals are cleared for next time.
-  __threadfence();
-  constexpr int PER = kTkBins / kTkThreads;
-  uint32_t cnt[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) cnt[k] = gh[k * kTkThreads + tid];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    h[k * kTkThreads + tid] = cnt[k];
-    gh[k * kTkThreads + tid] = 0;
-  }
-  __syncthreads();
-  int b1, above;
-  find_digit(h, kTkBins, K, tmp, res, b1, above);
-  if (tid == 0) {
-    sc.sel[4 * i + 0] = b1;
-    sc.sel[4 * i + 1] = above;
-    sc.done[i] = 0;
-  }
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
 }
 
-__global__ __launch_bounds__(kTkThreads) void k_topk_filter(const float* __restrict__ scores,
-                                                            int64_t stride,
-                                                            const int32_t* __restrict__ req_ids,
-                                                            StateView v, TkScratch sc) {
-  __shared__ int tmp[kTkThreads / 64 + 1];
-  const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+__device__ inline int wave_incl_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kTkThreads) void k_topk_filter(const float* __restrict__ scores, int64_t stride,
+                                                            const int32_t* __restrict__ req_ids, StateView v,
+                                                            TkScratch sc) {
+  constexpr int NW = kTkThreads / 64;
+  constexpr int PER_WAVE = kTkChunk / NW;  // 512 scores per wave
+  constexpr int NU = PER_WAVE / 256;       // float4 loads per lane
+  __shared__ int wcount[NW];
+  __shared__ uint32_t wmax[NW];
+  const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = request_of(req_ids, i, v);
   if (r < 0) return;
-  const int L = v.ctx_len[r], K = v.top_k;
-  if (L <= K) return;
+  const int L = v.ctx_len[r];
+  if (L <= v.top_k) return;
   const int nch = (L + kTkChunk - 1) / kTkChunk;
   if (c >= nch) return;
-  const uint32_t b1 = (uint32_t)sc.sel[4 * i];
-  constexpr int EPT = kTkChunk / kTkThreads;  // consecutive scores per thread
-  const int t0 = c * kTkChunk + tid * EPT;
   const float* s = scores + (size_t)i * stride;
-  uint32_t key[EPT];
-  int keep = 0;
-  if (t0 + EPT <= L) {
+  const uint32_t thr = sc.bound[r];
+  const int beg = c * kTkChunk + wave * PER_WAVE, end = min(L, beg + PER_WAVE);
+  float4 x[NU];
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(s + t0 + e);
-      key[e] = score_key(x.x);
-      key[e + 1] = score_key(x.y);
-      key[e + 2] = score_key(x.z);
-      key[e + 3] = score_key(x.w);
+  for (int u = 0; u < NU; ++u) {
+    const int t = beg + 256 * u + 4 * lane;
+    if (t + 4 <= end) {
+      x[u] = *reinterpret_cast<const float4*>(s + t);
+    } else {
+      x[u].x = t < end ? s[t] : 0.f;
+      x[u].y = t + 1 < end ? s[t + 1] : 0.f;
+      x[u].z = t + 2 < end ? s[t + 2] : 0.f;
+      x[u].w = 0.f;
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) key[e] = (t0 + e < L) ? score_key(s[t0 + e]) : 0u;
   }
+  uint32_t k[NU][4];
+  unsigned long long b[NU][4];
+  int run = 0;
+  uint32_t mx = 0u;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) keep += (t0 + e < L && (key[e] >> 20) >= b1) ? 1 : 0;
-  int total;
-  int pos = block_excl_sum(keep, tmp, total);
-  uint2* out = sc.cand + ((size_t)i * sc.max_chunks + c) * kTkChunk;
+  for (int u = 0; u < NU; ++u) {
+    const int t = beg + 256 * u + 4 * lane;
+    k[u][0] = score_key(x[u].x);
+    k[u][1] = score_key(x[u].y);
+    k[u][2] = score_key(x[u].z);
+    k[u][3] = score_key(x[u].w);
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (t0 + e < L && (key[e] >> 20) >= b1) out[pos++] = make_uint2(key[e], (uint32_t)(t0 + e));
+    for (int e = 0; e < 4; ++e) {
+      const bool f = t + e < end && k[u][e] >= thr;
+      b[u][e] = __ballot(f);
+      run += __popcll(b[u][e]);
+      mx = f ? max(mx, k[u][e]) : mx;
+    }
   }
-  if (tid == 0) sc.count[(size_t)i * sc.max_chunks + c] = total;
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    wcount[wave] = run;
+    wmax[wave] = mx;
+  }
+  __syncthreads();
+  int before = 0, total = 0;
+  uint32_t cmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? wcount[w] : 0;
+    total += wcount[w];
+    cmax = max(cmax, wmax[w]);
+  }
+  // token order inside the wave: t = beg + 256u + 4 lane + e, so the rank of
+  // element (u, e) of this lane counts all of u' < u, then lanes below this
+  // one over every e, then e' < e of this lane
+  uint2* dst = sc.cand + ((size_t)i * sc.max_chunks + c) * kTkChunk + before;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int pos = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = beg + 256 * u + 4 * lane;
+    int p = pos + __popcll(b[u][0] & below) + __popcll(b[u][1] & below) + __popcll(b[u][2] & below) +
+            __popcll(b[u][3] & below);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((b[u][e] >> lane) & 1ull) dst[p++] = make_uint2(k[u][e], (uint32_t)(t + e));
+    pos += __popcll(b[u][0]) + __popcll(b[u][1]) + __popcll(b[u][2]) + __popcll(b[u][3]);
+  }
+  if (tid == 0) {
+    sc.count[(size_t)i * sc.max_chunks + c] = total;
+    sc.maxk[(size_t)i * sc.max_chunks + c] = cmax;
+  }
 }
 
-// Locate survivor v (0-based, in index order) among the chunk slices.
-__device__ inline uint2 survivor(const uint2* cand, const int* off, int nch, int v) {
-  int lo = 0, hi = nch;  // off[lo] <= v < off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (off[mid] <= v) lo = mid; else hi = mid;
+// Block-wide search of a 4096-bin histogram from the top bin down: for each
+// of two needs (1 <= need <= total), the bin b with above(b) < need <=
+// above(b) + h[b], and above(b). Every thread gets the results.
+struct FindOut {
+  int b[2];
+  int above[2];
+};
+__device__ void hist_find2(const uint32_t* h, int need0, int need1, int* wtot, FindOut* res, FindOut& out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = kTkBins - 1 - 4 * tid;  // this thread's bins hi, hi-1, hi-2, hi-3
+  const uint4 q = *reinterpret_cast<const uint4*>(h + hi - 3);
+  const int c4 = (int)(q.x + q.y + q.z + q.w);
+  const int incl_w = wave_incl_sum(c4);
+  if (lane == 63) wtot[wave] = incl_w;
+  __syncthreads();
+  int pre = 0;
+#pragma unroll
+  for (int w = 0; w < kTkSelWaves; ++w) pre += w < wave ? wtot[w] : 0;
+  const int incl = pre + incl_w, excl = incl - c4;
+  const int need[2] = {need0, need1};
+#pragma unroll
+  for (int z = 0; z < 2; ++z) {
+    if (excl < need[z] && need[z] <= incl) {
+      const int cnt[4] = {(int)q.w, (int)q.z, (int)q.y, (int)q.x};  // bins hi .. hi-3
+      int above = excl, bb = hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bb == hi - e && above + cnt[e] < need[z]) {
+          above += cnt[e];
+          bb = hi - e - 1;
+        }
+      }
+      res->b[z] = bb;
+      res->above[z] = above;
+    }
   }
-  return cand[(size_t)lo * kTkChunk + (v - off[lo])];
+  __syncthreads();
+  out = *res;
 }
 
-__global__ __launch_bounds__(kTkFinalThreads) void k_topk_final(const int32_t* __restrict__ req_ids,
-                                                                StateView v, TkScratch sc,
-                                                                int32_t* __restrict__ idx_out) {
-  __shared__ uint32_t h[kTkBins];
+__global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __restrict__ scores, int64_t stride,
+                                                               const int32_t* __restrict__ req_ids, StateView v,
+                                                               TkScratch sc, int32_t* __restrict__ idx_out) {
+  constexpr int NW = kTkSelWaves;
+  __shared__ __align__(16) uint32_t hist[3][kTkBins];
   __shared__ int off[kTkMaxChunks + 1];
-  __shared__ uint2 surv[kTkFinalStage];
-  __shared__ int tmp[kTkFinalThreads / 64 + 1];
-  __shared__ int res[2];
+  __shared__ uint2 surv[kTkStage];
+  __shared__ int wtot[NW];
+  __shared__ int weq[NW];
+  __shared__ uint32_t wmax[NW];
+  __shared__ FindOut fres;
   const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = v.top_k;
   int32_t* out = idx_out + (size_t)i * K;
   const int r = request_of(req_ids, i, v);
-  const int L = r < 0 ? 0 : v.ctx_len[r];
+  if (r < 0) {
+    if (tid == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, (uint32_t)req_ids[i]);
+    for (int j = tid; j < K; j += kTkSelThreads) out[j] = -1;
+    return;
+  }
+  const int L = v.ctx_len[r];
   if (L <= K) {  // every token is selected
-    for (int j = tid; j < K; j += kTkFinalThreads) out[j] = j < L ? j : -1;
+    for (int j = tid; j < K; j += kTkSelThreads) out[j] = j < L ? j : -1;
     return;
   }
   const int nch = (L + kTkChunk - 1) / kTkChunk;
-  // chunk offsets of the survivors (exclusive prefix over chunk counts)
+  const float* s = scores + (size_t)i * stride;
+  const uint2* cand = sc.cand + (size_t)i * sc.max_chunks * kTkChunk;
+  const int32_t* cnt = sc.count + (size_t)i * sc.max_chunks;
+  const uint32_t* cmx = sc.maxk + (size_t)i * sc.max_chunks;
+  const uint32_t thr = sc.bound[r];
+
+  // 1. chunk offsets of the survivors, their count and largest key
+  for (int b = tid; b < 3 * kTkBins; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
   int run = 0;
-  for (int base = 0; base < nch; base += kTkFinalThreads) {
-    const int c = base + tid;
-    const int x = c < nch ? sc.count[(size_t)i * sc.max_chunks + c] : 0;
+  uint32_t mx = 0u;
+  for (int base = 0; base < nch; base += kTkSelThreads) {
+    const int cc = base + tid;
+    const int x = cc < nch ? cnt[cc] : 0;
+    mx = max(mx, cc < nch ? cmx[cc] : 0u);
     int tot;
-    const int e = block_excl_sum(x, tmp, tot);
-    if (c < nch) off[c] = run + e;
+    const int e = block_excl_sum(x, wtot, tot);
+    if (cc < nch) off[cc] = run + e;
     run += tot;
   }
+  mx = wave_max_u32(mx);
+  if (lane == 0) wmax[wave] = mx;
   if (tid == 0) off[nch] = run;
   __syncthreads();
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) kmax = max(kmax, wmax[w]);
   const int total = run;
-  const uint2* cand = sc.cand + (size_t)i * sc.max_chunks * kTkChunk;
-  // Survivors in index order: staged in LDS when they fit (one wave copies
-  // one chunk slice), otherwise read from the chunk slices in place.
-  const bool staged = total <= kTkFinalStage;
+  const bool raw = total < K;  // fewer than K passed: select over the raw scores
+  const bool staged = !raw && total <= kTkStage;
+  const int n = raw ? L : total;
+  const uint32_t base = raw ? 0u : thr;
+  const uint32_t range = raw ? 0xFFFFFFFFu : kmax - base;
+  const int B = range == 0u ? 0 : 32 - __clz(range);  // bits of (key - base)
+  const int s1 = B > 12 ? B - 12 : 0;
+
+  // survivor x (0 <= x < n) in token order
+  auto get = [&](int x) -> uint2 {
+    if (staged) return surv[x];
+    if (raw) return make_uint2(score_key(s[x]), (uint32_t)x);
+    int lo = 0, hi = nch;  // off[lo] <= x < off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= x) lo = mid; else hi = mid;
+    }
+    return cand[(size_t)lo * kTkChunk + (x - off[lo])];
+  };
+
+  // 2. first digit (bits s1 .. B-1 of key - base), staging into LDS on the way
   if (staged) {
-    for (int c = wave; c < nch; c += kTkFinalThreads / 64) {
-      const int o = off[c], n = off[c + 1] - o;
-      for (int j = lane; j < n; j += 64) surv[o + j] = cand[(size_t)c * kTkChunk + j];
+    constexpr int U = 4;
+    for (int x0 = tid; x0 < n; x0 += U * kTkSelThreads) {
+      uint2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int x = x0 + u * kTkSelThreads;
+        if (x < n) {
+          int lo = 0, hi = nch;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (off[mid] <= x) lo = mid; else hi = mid;
+          }
+          e[u] = cand[(size_t)lo * kTkChunk + (x - off[lo])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int x = x0 + u * kTkSelThreads;
+        if (x < n) {
+          surv[x] = e[u];
+          atomicAdd(&hist[0][(e[u].x - base) >> s1], 1u);
+        }
+      }
+    }
+  } else {
+    for (int x = tid; x < n; x += kTkSelThreads) atomicAdd(&hist[0][(get(x).x - base) >> s1], 1u);
+  }
+  __syncthreads();
+  FindOut f;
+  hist_find2(hist[0], K, min(n, K + K / 4), wtot, &fres, f);
+  uint32_t pre = (uint32_t)f.b[0];
+  int need = K - f.above[0];
+  const int bn = f.b[1];
+  // 3. lower digits (at most two more: 12 + 12 + 8 bits)
+  int sh = s1;
+  for (int pass = 1; sh > 0; ++pass) {
+    const int w = sh > 12 ? 12 : sh;
+    const int sn = sh - w;
+    const uint32_t mask = (1u << w) - 1u;
+    uint32_t* h = hist[pass];
+    for (int x = tid; x < n; x += kTkSelThreads) {
+      const uint32_t rel = get(x).x - base;
+      if ((rel >> sh) == pre) atomicAdd(&h[(rel >> sn) & mask], 1u);
     }
     __syncthreads();
+    FindOut g;
+    hist_find2(h, need, need, wtot, &fres, g);
+    pre = (pre << w) | (uint32_t)g.b[0];
+    need -= g.above[0];
+    sh = sn;
   }
-  auto get = [&](int x) -> uint2 { return staged ? surv[x] : survivor(cand, off, nch, x); };
-  const uint32_t b1 = (uint32_t)sc.sel[4 * i];
-  const int need1 = K - sc.sel[4 * i + 1];
-  // pass 2: bits 19..8 of the keys whose top digit is b1
-  for (int b = tid; b < kTkBins; b += kTkFinalThreads) h[b] = 0;
-  __syncthreads();
-  for (int x = tid; x < total; x += kTkFinalThreads) {
-    const uint2 kv = get(x);
-    if ((kv.x >> 20) == b1) atomicAdd(&h[(kv.x >> 8) & 0xFFFu], 1u);
+  const uint32_t T = base + pre;
+  const int ties = need;  // keys equal to T that are taken
+  // 4. ordered output: wave w walks survivors [w q, (w + 1) q) in order
+  const int q = (n + NW - 1) / NW;
+  const int beg = min(n, wave * q), end = min(n, beg + q);
+  int gt = 0, eq = 0;
+  for (int x0 = beg; x0 < end; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t kv = x < end ? get(x).x : 0u;
+    gt += __popcll(__ballot(x < end && kv > T));
+    eq += __popcll(__ballot(x < end && kv == T));
+  }
+  __syncthreads();  // wtot is reused
+  if (lane == 0) {
+    wtot[wave] = gt;
+    weq[wave] = eq;
   }
   __syncthreads();
-  int b2, above2;
-  find_digit(h, kTkBins, need1, tmp, res, b2, above2);
-  const int need2 = need1 - above2;
-  // pass 3: bits 7..0 of the keys whose top 24 bits are (b1, b2)
-  const uint32_t pre24 = (b1 << 12) | (uint32_t)b2;
-  for (int b = tid; b < kTkBins; b += kTkFinalThreads) h[b] = 0;
-  __syncthreads();
-  for (int x = tid; x < total; x += kTkFinalThreads) {
-    const uint2 kv = get(x);
-    if ((kv.x >> 8) == pre24) atomicAdd(&h[kv.x & 0xFFu], 1u);
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    gt_before += w < wave ? wtot[w] : 0;
+    eq_before += w < wave ? weq[w] : 0;
   }
-  __syncthreads();
-  int b3, above3;
-  find_digit(h, kTkBins, need2, tmp, res, b3, above3);
-  const int ties = need2 - above3;  // how many keys equal to T are taken
-  const uint32_t T = (pre24 << 8) | (uint32_t)b3;
-  // ordered compaction of the selected survivors
-  int sel_run = 0, tie_run = 0;
-  for (int base = 0; base < total; base += kTkFinalThreads) {
-    const int x = base + tid;
-    uint2 kv = make_uint2(0u, 0u);
-    if (x < total) kv = get(x);
-    const bool eq = x < total && kv.x == T;
-    int eq_tot;
-    const int tie_rank = tie_run + block_excl_count(eq, tmp, eq_tot);
-    const bool sel = x < total && (kv.x > T || (eq && tie_rank < ties));
-    int sel_tot;
-    const int pos = sel_run + block_excl_count(sel, tmp, sel_tot);
-    if (sel) out[pos] = (int32_t)kv.y;
-    sel_run += sel_tot;
-    tie_run += eq_tot;
+  int pos = gt_before + min(eq_before, ties);
+  int tie_run = eq_before;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int x0 = beg; x0 < end; x0 += 64) {
+    const int x = x0 + lane;
+    uint2 e = make_uint2(0u, 0u);
+    if (x < end) e = get(x);
+    const bool is_eq = x < end && e.x == T;
+    const unsigned long long beq = __ballot(is_eq);
+    const int tie_rank = tie_run + __popcll(beq & below);
+    const bool sel = x < end && (e.x > T || (is_eq && tie_rank < ties));
+    const unsigned long long bs = __ballot(sel);
+    const int at = pos + __popcll(bs & below);
+    if (sel && at < K) out[at] = (int32_t)e.y;
+    pos += __popcll(bs);
+    tie_run += __popcll(beq);
+  }
+  // 5. the bound for the next call
+  if (tid == 0) {
+    uint32_t nb;
+    if (n >= K + K / 4) {
+      nb = base + ((uint32_t)bn << s1);
+    } else {
+      const uint32_t d = (T - base) + (1u << s1);
+      nb = base > d ? base - d : 0u;
+    }
+    sc.bound[r] = nb;
   }
 }
 
@@ -275,16 +382,13 @@ hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int
                       int32_t n_req, int32_t* idx_out, hipStream_t s) {
   StateView v = make_view(p);
   TkScratch sc;
-  sc.hist = reinterpret_cast<uint32_t*>(p->state + p->off.tk_hist);
-  sc.done = reinterpret_cast<uint32_t*>(p->state + p->off.tk_done);
-  sc.sel = reinterpret_cast<int32_t*>(p->state + p->off.tk_sel);
   sc.count = reinterpret_cast<int32_t*>(p->state + p->off.tk_count);
+  sc.maxk = reinterpret_cast<uint32_t*>(p->state + p->off.tk_max);
   sc.cand = reinterpret_cast<uint2*>(p->state + p->off.tk_cand);
+  sc.bound = reinterpret_cast<uint32_t*>(p->state + p->off.tk_bound);
   sc.max_chunks = (p->d.max_context + kTkChunk - 1) / kTkChunk;
-  const dim3 grid(sc.max_chunks, n_req);
-  k_topk_hist<<<grid, kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc);
-  k_topk_filter<<<grid, kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc);
-  k_topk_final<<<n_req, kTkFinalThreads, 0, s>>>(req_ids, v, sc, idx_out);
+  k_topk_filter<<<dim3(sc.max_chunks, n_req), kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc);
+  k_topk_select<<<n_req, kTkSelThreads, 0, s>>>(scores, stride, req_ids, v, sc, idx_out);
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
 }

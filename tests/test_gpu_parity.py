@@ -233,3 +233,36 @@ def test_device_error_on_index_past_context():
         assert rn.pool.device_error()[0] == 0
     finally:
         rn.close()
+
+
+def test_topk_both_paths_in_one_batch():
+    """Contexts on both sides of the one-workgroup limit (256K tokens) in one
+    call: the single-workgroup and the multi-workgroup kernels each take
+    their requests, with ties, -0.0 and an empty request."""
+    rng = np.random.default_rng(5)
+    max_ctx, K = 300000, 2048
+    lens = [300000, 262145, 262144, 70001, 0, 290000]
+    R = len(lens)
+    pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=R, max_context=max_ctx,
+                      kv_dtype="bf16", top_k=K, hot_rows=4096, max_batch=R, max_q_rows=16,
+                      host_rows=R * max_ctx)
+    try:
+        stride = 300032
+        sc = rng.standard_normal((R, stride)).astype(np.float32)
+        sc[1, ::7] = np.float32(2.5)          # many ties near the threshold
+        sc[2] = np.round(sc[2] * 4) / 4       # coarse values: heavy ties
+        sc[3, ::5] = -0.0
+        sc[5] = 1.0                            # all equal
+        for r, L in enumerate(lens):
+            pool.set_residency(r, L, r * max_ctx, None)
+        d_sc = torch.from_numpy(sc).cuda()
+        req = torch.arange(R, dtype=torch.int32, device="cuda")
+        idx = torch.full((R, K), -5, dtype=torch.int32, device="cuda")
+        for rep in range(2):
+            pool.select_topk(d_sc, req, idx)
+            got = idx.cpu().numpy()
+            for r, L in enumerate(lens):
+                assert np.array_equal(got[r], select_topk(sc[r], L, K)), f"req {r} L={L} rep {rep}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
