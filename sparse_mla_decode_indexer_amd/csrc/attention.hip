@@ -344,34 +344,51 @@ __global__ __launch_bounds__(kAttThreads) void k_attn_mfma(
 }
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
-__global__ __launch_bounds__(256) void k_attn_combine(int n_rows, int QR, int n_splits,
-                                                      const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_lse,
-                                                      float* __restrict__ out, float* __restrict__ lse_out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// Thread (row, 4 dims): all of its partial loads are in flight together.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, int QR, int n_splits,
+                                                                  const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_lse,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ lse_out) {
+  const int g = blockIdx.x * kCombineThreads + threadIdx.x;
+  const int row = g / (kNope / 4), d4 = g - row * (kNope / 4);
   if (row >= n_rows) return;
   const int i = row / QR, qh = row - i * QR;
+  const size_t base = (size_t)i * n_splits * QR + qh;  // partial row of split s: base + s * QR
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_lse[((size_t)i * n_splits + s) * QR + qh]);
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_lse[base + (size_t)s * QR]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t pr = ((size_t)i * n_splits + s) * QR + qh;
-      const float w = __builtin_amdgcn_exp2f(part_lse[pr] - M);
-      W += w;
-      const float4 a = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane);
-      const float4 b = *reinterpret_cast<const float4*>(part_o + pr * kNope + 8 * lane + 4);
-      o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
-      o[4] += w * b.x; o[5] += w * b.y; o[6] += w * b.z; o[7] += w * b.w;
+    int s = 0;
+    for (; s + 4 <= n_splits; s += 4) {
+      float w[4];
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t pr = base + (size_t)(s + u) * QR;
+        w[u] = part_lse[pr];
+        x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float e = __builtin_amdgcn_exp2f(w[u] - M);
+        W += e;
+        o.x += e * x[u].x; o.y += e * x[u].y; o.z += e * x[u].z; o.w += e * x[u].w;
+      }
+    }
+    for (; s < n_splits; ++s) {
+      const size_t pr = base + (size_t)s * QR;
+      const float e = __builtin_amdgcn_exp2f(part_lse[pr] - M);
+      const float4 x = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
+      W += e;
+      o.x += e * x.x; o.y += e * x.y; o.z += e * x.z; o.w += e * x.w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  float* d = out + (size_t)row * kNope + 8 * lane;
-  *reinterpret_cast<float4*>(d) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-  *reinterpret_cast<float4*>(d + 4) = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
-  if (lse_out && lane == 0) lse_out[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
+  reinterpret_cast<float4*>(out + (size_t)row * kNope)[d4] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (lse_out && d4 == 0) lse_out[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 
 // fp32 rows and queries: one workgroup per query row, vector-unit fp32.
@@ -496,7 +513,9 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
                                                    part_o, part_lse, err);
   if (splits > 1) {
     const int rows = n_req * QR;
-    k_attn_combine<<<(rows + 3) / 4, 256, 0, s>>>(rows, QR, splits, part_o, part_lse, out, lse_out);
+    const int64_t threads = (int64_t)rows * (kNope / 4);
+    k_attn_combine<<<(int)((threads + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
+        rows, QR, splits, part_o, part_lse, out, lse_out);
   }
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;

@@ -11,13 +11,18 @@
 //     and rewrites the LRU order with ordered compactions in LDS, updates
 //     tags / stamps / reverse map, writes the plan and the counts, and
 //     publishes the plan with a per-request flag;
-//   copy workgroup (request i, part c), one per 64 plan positions: reads the
-//     page table and reverse map itself to guess which of its tokens miss
-//     and starts reading those rows from the mapped host store over PCIe
-//     right away, then waits for the flag and writes the rows the
-//     bookkeeper actually classified as misses into their hot slots (rows it
-//     did not guess are read then). The guess only decides how early the
-//     PCIe reads start; which rows are written comes from the bookkeeper.
+//   copy workgroup (request i, part c), one per 16 plan positions (4 per
+//     wave): reads the page table and reverse map itself to guess which of
+//     its tokens miss and starts reading those rows from the mapped host
+//     store over PCIe right away, then waits for the flag and writes the
+//     rows the bookkeeper actually classified as misses into their hot
+//     slots (rows it did not guess are read then). The guess only decides
+//     how early the PCIe reads start; which rows are written comes from the
+//     bookkeeper.
+// Bookkeeper thread t owns plan positions [tP, tP + P) and LRU positions
+// [tQ, tQ + Q) (P, Q powers of two), so each ordered compaction is one
+// block-wide scan; every table lookup of a phase is issued before any is
+// used.
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
 // bounded (a device error is raised past the bound and the copy skipped).
@@ -40,7 +45,7 @@ namespace hs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RsScratch {
-  unsigned long long* miss_mask;  // [batch][parts] miss bits of 64 plan positions
+  unsigned long long* miss_mask;  // [batch][words] miss bits of 64 plan positions
   uint32_t* flag;                 // [batch] 1 once request i's plan is published
   uint32_t* exit_cnt;             // [batch] copy workgroups of request i done
   uint32_t* ticket;               // [2] roles handed out, workgroups exited
@@ -49,15 +54,17 @@ struct RsScratch {
 };
 
 enum : int { kPad = 0, kRes = 1, kHot = 2, kMiss = 3 };
-constexpr int kRsMaxIt = kMaxTopK / kRsThreads;  // top-K entries per thread
 constexpr int kRsWaves = kRsThreads / 64;
-constexpr int kSpinLimit = 1 << 20;  // polls of the flag (>= 0.1 s) before giving up
-constexpr int kRsPart = 64;          // plan positions per copy workgroup (divides 64)
+constexpr int kRsPos = kMaxTopK / kRsThreads;      // plan positions per bookkeeper thread, at most
+constexpr int kRsSlots = kMaxHotRows / kRsThreads;  // LRU positions per bookkeeper thread, at most
+constexpr int kRsPart = 4 * kRsWaves;              // plan positions per copy workgroup
+constexpr int kSpinLimit = 1 << 20;                // polls of the flag (>= 0.1 s) before giving up
 
 struct RsArgs {
   const int32_t* idx;
   const int32_t* req_ids;
   int n_req;
+  int P, Q;  // plan and LRU positions per bookkeeper thread
   int32_t* plan_out;
   int32_t* counts_out;
   const uint8_t* host_rows;
@@ -66,21 +73,29 @@ struct RsArgs {
   float* pool_scales;
 };
 
-struct RsShared {
-  int32_t lru[kMaxHotRows];
-  int32_t comp[kMaxHotRows];
-  uint8_t flag[kMaxHotRows];  // bit0: hit this step, bit1: victim
+struct RsStatic {
   int tmp[kRsWaves + 1];
-  int32_t tok[64];            // copy role: token of each position, -1 = not guessed
-  int8_t gpos[64];            // copy role: positions of the guessed misses, in order
-  int n_guess;
+  unsigned long long mword[kMaxTopK / 64];
+  int n_res, n_hot;
   int role;
   int go;
 };
 
-__device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, const RsScratch& sc, RsShared& sh, int i) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = v.top_k, S = v.hot_rows, ps = v.page_size, lps = v.log2_ps;
+// Dynamic LDS of a bookkeeper: lru[S] (reused for the victims), tag[S] and
+// hot_pages[S / page_size] int32, flag[S] uint8 (bit0: hit this step, bit1:
+// victim).
+__host__ __device__ inline size_t rs_dyn_bytes(int S, int HP) {
+  return 8 * (size_t)S + 4 * (size_t)HP + (size_t)S;
+}
+
+// The bookkeeper issues every global load before its first global store:
+// the vector memory counter counts stores too, so a load waited for after
+// a store would also wait for that store to complete.
+__device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, const RsScratch& sc, RsStatic& st,
+                                         unsigned char* dyn, int i) {
+  const int tid = threadIdx.x;
+  const int K = v.top_k, S = v.hot_rows, ps = v.page_size, lps = v.log2_ps, HP = v.hot_pages_per_req;
+  const int P = a.P, Q = a.Q;
   const int32_t* sel = a.idx + (size_t)i * K;
   int32_t* plan = a.plan_out + (size_t)i * K;
   const int r0 = a.req_ids[i];
@@ -107,113 +122,160 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   int32_t* tag = v.slot_tag + (size_t)r * S;
   int32_t* stamp = v.slot_stamp + (size_t)r * S;
   int32_t* order = v.lru_order + (size_t)r * S;
-  const int32_t* hp = v.hot_pages + (size_t)r * v.hot_pages_per_req;
-  for (int s = tid; s < S; s += kRsThreads) {
-    sh.flag[s] = 0;
-    sh.lru[s] = order[s];
-  }
-  __syncthreads();
+  const int32_t* hp_g = v.hot_pages + (size_t)r * HP;
+  int32_t* lru = reinterpret_cast<int32_t*>(dyn);
+  int32_t* vic = lru;  // the victims, once every thread holds its LRU slice
+  int32_t* tag_l = lru + S;
+  int32_t* hp = tag_l + S;
+  uint8_t* flag = reinterpret_cast<uint8_t*>(hp + HP);
 
-  // 1. classify, stamp the hits, rank the misses in token order
-  int kind[kRsMaxIt], tok[kRsMaxIt], prow[kRsMaxIt], mrank[kRsMaxIt];
-  int M = 0, n_res = 0, n_hot = 0;
+  // 0. loads: LRU order, slot tags, hot pages (to LDS); this thread's
+  //    selected tokens, then their page-table and reverse-map entries
+  for (int s = tid; s < S; s += kRsThreads) {
+    lru[s] = order[s];
+    tag_l[s] = tag[s];
+    flag[s] = 0;
+  }
+  for (int p = tid; p < HP; p += kRsThreads) hp[p] = hp_g[p];
+  for (int w = tid; w < sc.words; w += kRsThreads) st.mword[w] = 0ull;
+  if (tid == 0) st.n_res = st.n_hot = 0;
+  int tok[kRsPos], code[kRsPos];  // code: pool row, -1 nothing, -2 miss
+  int M, mbase;
+  {
+    int g[kRsPos], slot[kRsPos];
 #pragma unroll
-  for (int it = 0; it < kRsMaxIt; ++it) {
-    kind[it] = kPad;
-    tok[it] = -1;
-    prow[it] = -1;
-    mrank[it] = 0;
-    if (it * kRsThreads >= K) continue;  // uniform across the block
-    const int j = it * kRsThreads + tid;
-    if (j < K) {
-      const int t = sel[j];
-      tok[it] = t;
-      const bool ok = t >= 0 && t < L;
-      if (t >= L) raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)t);
-      // both lookups issued before either is used
-      const int g = ok ? pt[t >> lps] : -1;
-      const int slot = ok ? rev[t] : -1;
-      if (ok) {
-        if (g >= 0) {
-          kind[it] = kRes;
-          prow[it] = g * ps + (t & (ps - 1));
-        } else if (slot >= 0) {
-          const int hpg = hp[slot >> lps];
-          if (hpg >= 0) {
-            kind[it] = kHot;
-            sh.flag[slot] = 1;
-            stamp[slot] = n;
-            prow[it] = hpg * ps + (slot & (ps - 1));
-          } else {
-            raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)slot);
-          }
+    for (int e = 0; e < kRsPos; ++e) {
+      const int j = tid * P + e;
+      tok[e] = (e < P && j < K) ? sel[j] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      const int t = tok[e];
+      const int tt = (t >= 0 && t < L) ? t : 0;  // in-range address either way
+      g[e] = pt[tt >> lps];
+      slot[e] = rev[tt];
+    }
+    __syncthreads();  // LDS tables ready
+    // 1. classify: resident > hot > miss (hit flags in LDS, no stores yet)
+    int nm = 0, nr = 0, nh = 0;
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      code[e] = -1;
+      const int j = tid * P + e;
+      const int t = tok[e];
+      if (!(e < P && j < K) || t < 0) continue;
+      if (t >= L) {
+        raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)t);
+      } else if (g[e] >= 0) {
+        code[e] = g[e] * ps + (t & (ps - 1));
+        ++nr;
+      } else if (slot[e] >= 0) {
+        const int sl = slot[e];
+        const int hpg = sl < S ? hp[sl >> lps] : -1;
+        if (hpg >= 0) {
+          flag[sl] = 1;
+          code[e] = hpg * ps + (sl & (ps - 1));
+          ++nh;
         } else {
-          kind[it] = kMiss;
+          raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)sl);
         }
+      } else {
+        code[e] = -2;
+        atomicOr(&st.mword[j >> 6], 1ull << (j & 63));
+        ++nm;
       }
     }
-    const unsigned long long mb = __ballot(kind[it] == kMiss);
-    if (lane == 0 && it * kRsThreads + 64 * wave < K) sc.miss_mask[(size_t)i * sc.words + it * kRsWaves + wave] = mb;
-    int tot;
-    mrank[it] = M + block_excl_count(kind[it] == kMiss, sh.tmp, tot);
-    M += tot;
-    n_res += __syncthreads_count(kind[it] == kRes);
-    n_hot += __syncthreads_count(kind[it] == kHot);
+    if (nr) atomicAdd(&st.n_res, nr);
+    if (nh) atomicAdd(&st.n_hot, nh);
+    mbase = block_excl_sum(nm, st.tmp, M);  // misses rank in token order
   }
-  // (the counting barriers above also publish the hit flags)
-
-  // 2. untouched slots in LRU order -> comp[0 .. S - |U|)
-  int kept = 0;
-  for (int base = 0; base < S; base += kRsThreads) {
-    const int s = base + tid < S ? sh.lru[base + tid] : -1;
-    const bool keep = s >= 0 && !(sh.flag[s] & 1);
-    int tot;
-    const int pos = kept + block_excl_count(keep, sh.tmp, tot);
-    if (keep) sh.comp[pos] = s;
-    kept += tot;
-  }
-  __syncthreads();
-  // 3. the first M untouched slots are the victims
-  for (int x = tid; x < M; x += kRsThreads) sh.flag[sh.comp[x]] |= 2;
-  __syncthreads();
-  // 4. new LRU order: remaining untouched slots, then hit and victim slots
-  //    in ascending slot number
-  for (int x = tid; x < kept - M; x += kRsThreads) order[x] = sh.comp[M + x];
-  int fresh = kept - M;
-  for (int base = 0; base < S; base += kRsThreads) {
-    const int s = base + tid;
-    const bool f = s < S && sh.flag[s] != 0;
-    int tot;
-    const int pos = fresh + block_excl_count(f, sh.tmp, tot);
-    if (f) order[pos] = s;
-    fresh += tot;
-  }
-  // 5. fill the victims with the misses (i-th miss -> i-th victim)
+  // 2. untouched slots in LRU order; the first M of them are the victims
+  int my[kRsSlots];
+  int kc = 0;
 #pragma unroll
-  for (int it = 0; it < kRsMaxIt; ++it) {
-    if (kind[it] != kMiss) continue;
-    const int t = tok[it];
-    const int slot = sh.comp[mrank[it]];
-    const int old = tag[slot];
-    if (old >= 0 && old < v.max_context) rev[old] = -1;
-    tag[slot] = t;
-    rev[t] = slot;
-    stamp[slot] = n;
-    const int hpg = hp[slot >> lps];
-    if (hpg >= 0) {
-      prow[it] = hpg * ps + (slot & (ps - 1));
-    } else {
-      raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)slot);
+  for (int e = 0; e < kRsSlots; ++e) {
+    const int x = tid * Q + e;
+    const int s = (e < Q && x < S) ? lru[x] : -1;
+    my[e] = (s >= 0 && !(flag[s] & 1)) ? s : -1;
+    kc += my[e] >= 0 ? 1 : 0;
+  }
+  int kept;
+  const int kbase = block_excl_sum(kc, st.tmp, kept);  // (its barriers end the reads of lru)
+  {
+    int kpos = kbase;
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (my[e] >= 0) {
+        if (kpos < M) {
+          vic[kpos] = my[e];
+          flag[my[e]] |= 2;
+        }
+        ++kpos;
+      }
     }
   }
-  // 6. plan; publish it to the copy workgroups; counts and step
+  __syncthreads();
+  // 3. stores. New LRU order: the untouched non-victims in their order,
+  //    then the hit and victim slots in ascending slot number, which all
+  //    take stamp n. Victims lose their old token.
+  {
+    int kpos = kbase;
 #pragma unroll
-  for (int it = 0; it < kRsMaxIt; ++it) {
-    const int j = it * kRsThreads + tid;
-    if (j < K) plan[j] = prow[it];
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (my[e] >= 0) {
+        if (kpos >= M) {
+          order[kpos - M] = my[e];
+        } else {
+          const int old = tag_l[my[e]];
+          if (old >= 0 && old < v.max_context) rev[old] = -1;
+        }
+        ++kpos;
+      }
+    }
   }
+  int fc = 0;
+#pragma unroll
+  for (int e = 0; e < kRsSlots; ++e) {
+    const int s = tid * Q + e;
+    fc += (e < Q && s < S && flag[s] != 0) ? 1 : 0;
+  }
+  int ftot;
+  int fpos = (kept - M) + block_excl_sum(fc, st.tmp, ftot);
+#pragma unroll
+  for (int e = 0; e < kRsSlots; ++e) {
+    const int s = tid * Q + e;
+    if (e < Q && s < S && flag[s] != 0) {
+      order[fpos++] = s;
+      stamp[s] = n;
+    }
+  }
+  // fill the victims with the misses (i-th miss -> i-th victim)
+  int mr = mbase;
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) {
+    if (code[e] != -2) continue;
+    const int t = tok[e];
+    const int vs = vic[mr++];
+    tag[vs] = t;
+    rev[t] = vs;
+    const int hpg = hp[vs >> lps];
+    if (hpg >= 0) {
+      code[e] = hpg * ps + (vs & (ps - 1));
+    } else {
+      code[e] = -1;
+      raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)vs);
+    }
+  }
+  // 4. plan and miss words; publish them to the copy workgroups; counts
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) {
+    const int j = tid * P + e;
+    if (e < P && j < K) plan[j] = code[e] < 0 ? -1 : code[e];
+  }
+  for (int w = tid; w < sc.words; w += kRsThreads) sc.miss_mask[(size_t)i * sc.words + w] = st.mword[w];
   publish();
   if (tid == 0) {
+    const int n_res = st.n_res, n_hot = st.n_hot;
     if (a.counts_out) {
       a.counts_out[3 * i] = n_res;
       a.counts_out[3 * i + 1] = n_hot;
@@ -226,16 +288,16 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   }
 }
 
-// Copy the missed rows of plan positions [c kRsPart, (c + 1) kRsPart) of request i.
+// Copy the missed rows of plan positions [c kRsPart, (c + 1) kRsPart) of
+// request i; wave w takes 4 of them.
 template <int ROW_BYTES, bool FP8>
-__device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc, RsShared& sh, int i,
-                          int c) {
-  constexpr int CH = ROW_BYTES / 16;           // 16-byte chunks per row
-  constexpr int CPL = (CH + 63) / 64;          // chunks per lane
-  constexpr int RPW = (kRsPart + kRsWaves - 1) / kRsWaves;  // guessed rows per wave (at most)
+__device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc, RsStatic& st,
+                                          int i, int c) {
+  constexpr int CH = ROW_BYTES / 16;   // 16-byte chunks per row
+  constexpr int CPL = (CH + 63) / 64;  // chunks per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = v.top_k, lps = v.log2_ps;
-  const int j0 = kRsPart * c;
+  const int j0 = kRsPart * c + 4 * wave;
   const int r0 = a.req_ids[i];
   const bool valid_req = r0 >= 0 && r0 < v.max_requests;
   const int r = valid_req ? r0 : 0;
@@ -244,32 +306,27 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   // Guess the misses from the current tables. The bookkeeper may be
   // updating them meanwhile (atomic reads, any outcome is harmless): the
   // guess only decides which host reads start before the plan is known.
-  if (wave == 0) {
+  int t = -1;
+  bool guess = false;
+  if (lane < 4) {
     const int j = j0 + lane;
-    const int t = lane < kRsPart && j < K ? a.idx[(size_t)i * K + j] : -1;
-    bool guess = false;
+    t = j < K ? a.idx[(size_t)i * K + j] : -1;
     if (t >= 0 && t < L) {
       const int g = v.page_table[(size_t)r * v.pages_per_req + (t >> lps)];
       const int slot =
           __hip_atomic_load(&v.rev[(size_t)r * v.max_context + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       guess = g < 0 && slot < 0;
     }
-    const unsigned long long m = __ballot(guess);
-    sh.tok[lane] = guess ? t : -1;
-    if (guess) sh.gpos[__popcll(m & ((1ull << lane) - 1ull))] = (int8_t)lane;
-    if (lane == 0) sh.n_guess = __popcll(m);
   }
-  __syncthreads();
-  const int ng = sh.n_guess;
-  // wave w reads guessed rows w, w + kRsWaves, ... into registers
-  u32x4 x[RPW][CPL];
-  int pos_of[RPW];
+  const unsigned gb = (unsigned)(__ballot(guess) & 0xFull);
+  int tk[4];
 #pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int rank = k * kRsWaves + wave;
-    pos_of[k] = rank < ng ? sh.gpos[rank] : -1;
-    if (pos_of[k] >= 0) {
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + sh.tok[pos_of[k]]) * ROW_BYTES);
+  for (int k = 0; k < 4; ++k) tk[k] = __shfl(t, k, 64);
+  u32x4 x[4][CPL];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if ((gb >> k) & 1u) {
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * ROW_BYTES);
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
         if (lane + 64 * u < CH) x[k][u] = s4[lane + 64 * u];
@@ -284,41 +341,27 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
       if (++spins > kSpinLimit) break;
       __builtin_amdgcn_s_sleep(4);
     }
-    sh.go = spins <= kSpinLimit;
+    st.go = spins <= kSpinLimit;
     if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (!sh.go) return;
-  const unsigned long long part_bits = ~0ull >> (64 - kRsPart);
-  const unsigned long long am = (sc.miss_mask[(size_t)i * sc.words + (j0 >> 6)] >> (j0 & 63)) & part_bits;
-  unsigned long long gm = 0ull;
-  for (int k = 0; k < ng; ++k) gm |= 1ull << sh.gpos[k];
+  if (!st.go) return;
+  // (j0 is a multiple of 4, so the 4 bits lie in one mask word)
+  const unsigned am = (unsigned)((sc.miss_mask[(size_t)i * sc.words + (j0 >> 6)] >> (j0 & 63)) & 0xFull);
   const int32_t* plan = a.plan_out + (size_t)i * K + j0;
-  // rows that were guessed and are misses: from registers
 #pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int pos = pos_of[k];
-    const int dst = pos >= 0 && ((am >> pos) & 1ull) ? plan[pos] : -1;
-    if (dst >= 0) {
-      u32x4* d4 = reinterpret_cast<u32x4*>(a.pool_rows + (int64_t)dst * ROW_BYTES);
+  for (int k = 0; k < 4; ++k) {
+    if (!((am >> k) & 1u)) continue;
+    const int dst = plan[k];
+    if (dst < 0) continue;
+    u32x4* d4 = reinterpret_cast<u32x4*>(a.pool_rows + (int64_t)dst * ROW_BYTES);
+    if ((gb >> k) & 1u) {
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
         if (lane + 64 * u < CH) d4[lane + 64 * u] = x[k][u];
-    }
-  }
-  // misses that were not guessed (rare): read now
-  {
-    unsigned long long m = am & ~gm;
-    for (int rank = 0; m; ++rank) {
-      const int pos = __ffsll((long long)m) - 1;
-      m &= m - 1ull;
-      if (rank % kRsWaves != wave) continue;
-      const int dst = plan[pos];
-      if (dst < 0) continue;
-      const int t = a.idx[(size_t)i * K + j0 + pos];
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + t) * ROW_BYTES);
-      u32x4* d4 = reinterpret_cast<u32x4*>(a.pool_rows + (int64_t)dst * ROW_BYTES);
+    } else {  // a miss that was not guessed (rare): read it now
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * ROW_BYTES);
       u32x4 y[CPL];
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
@@ -328,29 +371,26 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) d4[lane + 64 * u] = y[u];
     }
   }
-  if (FP8 && tid < kRsPart) {  // one fp8 scale per missed row
-    const int pos = tid;
-    if ((am >> pos) & 1ull) {
-      const int dst = plan[pos];
-      const int t = a.idx[(size_t)i * K + j0 + pos];
-      if (dst >= 0) a.pool_scales[dst] = a.host_scales[hbase + t];
-    }
+  if (FP8 && lane < 4 && ((am >> lane) & 1u)) {  // one fp8 scale per missed row
+    const int dst = plan[lane];
+    if (dst >= 0) a.pool_scales[dst] = a.host_scales[hbase + t];
   }
 }
 
 template <int ROW_BYTES, bool FP8>
 __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, RsScratch sc) {
-  __shared__ RsShared sh;
+  __shared__ RsStatic st;
+  extern __shared__ __align__(16) unsigned char rs_dyn[];
   const int tid = threadIdx.x;
-  if (tid == 0) sh.role = (int)atomicAdd(&sc.ticket[0], 1u);
+  if (tid == 0) st.role = (int)atomicAdd(&sc.ticket[0], 1u);
   __syncthreads();
-  const int role = sh.role;
+  const int role = st.role;
   if (role < a.n_req) {
-    bookkeep(a, v, sc, sh, role);
+    bookkeep(a, v, sc, st, rs_dyn, role);
   } else {
     const int q = role - a.n_req;
     const int i = q / sc.parts, c = q - i * sc.parts;
-    copy_part<ROW_BYTES, FP8>(a, v, sc, sh, i, c);
+    copy_part<ROW_BYTES, FP8>(a, v, sc, st, i, c);
     __syncthreads();
     if (tid == 0 && atomicAdd(&sc.exit_cnt[i], 1u) == (uint32_t)(sc.parts - 1)) {
       sc.flag[i] = 0;  // every copy workgroup of request i has seen the flag
@@ -364,6 +404,12 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   }
 }
 
+static int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
 hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
                          int32_t* plan_out, int32_t* counts_out, hipStream_t s) {
   StateView v = make_view(p);
@@ -374,18 +420,22 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   sc.ticket = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);
   sc.words = (p->d.top_k + 63) / 64;
   sc.parts = (p->d.top_k + kRsPart - 1) / kRsPart;
-  RsArgs a{idx, req_ids, n_req, plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
+  RsArgs a{idx, req_ids, n_req,
+           pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
+           pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads),
+           plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
            p->host_scales, p->pool_rows, p->pool_scales};
+  const size_t dyn = (rs_dyn_bytes(v.hot_rows, v.hot_pages_per_req) + 15) & ~(size_t)15;
   const int grid = n_req * (1 + sc.parts);
   switch (p->d.kv_dtype) {
     case HS_F32:
-      k_resolve<2304, false><<<grid, kRsThreads, 0, s>>>(a, v, sc);
+      k_resolve<2304, false><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
     case HS_BF16:
-      k_resolve<1152, false><<<grid, kRsThreads, 0, s>>>(a, v, sc);
+      k_resolve<1152, false><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
     default:
-      k_resolve<576, true><<<grid, kRsThreads, 0, s>>>(a, v, sc);
+      k_resolve<576, true><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
   }
   HS_HIP_CHECK(hipGetLastError());
