@@ -23,7 +23,7 @@ constexpr int kTkMaxChunks = 2048; // => max_context <= 4,194,304
 constexpr int kTkStage = 8192;     // survivors staged in LDS by the select workgroup
 
 // resolve
-constexpr int kRsThreads = 256;
+constexpr int kRsThreads = 1024;
 
 // attention
 constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)

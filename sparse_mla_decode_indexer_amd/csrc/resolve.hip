@@ -20,9 +20,8 @@
 //     how early the PCIe reads start; which rows are written comes from the
 //     bookkeeper.
 // Bookkeeper thread t owns plan positions [tP, tP + P) and LRU positions
-// [tQ, tQ + Q) (P, Q powers of two), so each ordered compaction is one
-// block-wide scan; every table lookup of a phase is issued before any is
-// used.
+// [tQ, tQ + Q) (P, Q powers of two, Q >= 4), so each ordered compaction is
+// one block-wide scan.
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
 // bounded (a device error is raised past the bound and the copy skipped).
@@ -75,42 +74,54 @@ struct RsArgs {
 
 struct RsStatic {
   int tmp[kRsWaves + 1];
-  unsigned long long mword[kMaxTopK / 64];
+  uint32_t mword[kMaxTopK / 32];  // miss bits, 32 plan positions per word
   int n_res, n_hot;
   int role;
   int go;
 };
 
-// Dynamic LDS of a bookkeeper: lru[S] (reused for the victims), tag[S] and
-// hot_pages[S / page_size] int32, flag[S] uint8 (bit0: hit this step, bit1:
-// victim).
-__host__ __device__ inline size_t rs_dyn_bytes(int S, int HP) {
-  return 8 * (size_t)S + 4 * (size_t)HP + (size_t)S;
+// Dynamic LDS of a bookkeeper, with Spad = 256 Q >= S: lru[Spad] and
+// tag[Spad] int32 (padded with -1), victims[K] int32, hot_pages[HP] int32,
+// flag[Spad] uint8 (bit0: hit this step, bit1: victim).
+__host__ __device__ inline size_t rs_dyn_bytes(int Spad, int K, int HP) {
+  return 8 * (size_t)Spad + 4 * (size_t)K + 4 * (size_t)HP + (size_t)Spad;
 }
 
-// The bookkeeper issues every global load before its first global store:
-// the vector memory counter counts stores too, so a load waited for after
-// a store would also wait for that store to complete.
+// The bookkeeper issues every global load before its first global store
+// (the vector memory counter counts stores too, so a load waited for after
+// a store would also wait for that store), and keeps its loops free of
+// per-lane conditions: loop bounds are uniform, LDS tables are padded, and
+// each phase issues all of its LDS reads before using them.
 __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, const RsScratch& sc, RsStatic& st,
                                          unsigned char* dyn, int i) {
   const int tid = threadIdx.x;
   const int K = v.top_k, S = v.hot_rows, ps = v.page_size, lps = v.log2_ps, HP = v.hot_pages_per_req;
-  const int P = a.P, Q = a.Q;
+  const int P = a.P, Q = a.Q, Spad = Q * kRsThreads;
   const int32_t* sel = a.idx + (size_t)i * K;
   int32_t* plan = a.plan_out + (size_t)i * K;
   const int r0 = a.req_ids[i];
+  // What the copy workgroups read (plan, miss words, flag) is written with
+  // device-coherent stores; the flag goes out once this workgroup's stores
+  // of the rest have completed. The LRU state is written afterwards: no copy
+  // workgroup reads it, and the flag does not wait for it.
+  auto put = [](int32_t* p, int x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto put_word = [&](int w, unsigned long long x) {
+    __hip_atomic_store(&sc.miss_mask[(size_t)i * sc.words + w], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   auto publish = [&]() {
-    __threadfence();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    asm volatile("" ::: "memory");
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(&sc.flag[i], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&sc.flag[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if (r0 < 0 || r0 >= v.max_requests) {
     if (tid == 0) {
       raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, (uint32_t)r0);
       if (a.counts_out) a.counts_out[3 * i] = a.counts_out[3 * i + 1] = a.counts_out[3 * i + 2] = 0;
     }
-    for (int j = tid; j < K; j += kRsThreads) plan[j] = -1;
-    for (int w = tid; w < sc.words; w += kRsThreads) sc.miss_mask[(size_t)i * sc.words + w] = 0ull;
+    for (int j = tid; j < K; j += kRsThreads) put(&plan[j], -1);
+    for (int w = tid; w < sc.words; w += kRsThreads) put_word(w, 0ull);
     publish();
     return;
   }
@@ -124,156 +135,231 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   int32_t* order = v.lru_order + (size_t)r * S;
   const int32_t* hp_g = v.hot_pages + (size_t)r * HP;
   int32_t* lru = reinterpret_cast<int32_t*>(dyn);
-  int32_t* vic = lru;  // the victims, once every thread holds its LRU slice
-  int32_t* tag_l = lru + S;
-  int32_t* hp = tag_l + S;
+  int32_t* tag_l = lru + Spad;
+  int32_t* vic = tag_l + Spad;
+  int32_t* hp = vic + K;
   uint8_t* flag = reinterpret_cast<uint8_t*>(hp + HP);
 
-  // 0. loads: LRU order, slot tags, hot pages (to LDS); this thread's
-  //    selected tokens, then their page-table and reverse-map entries
-  for (int s = tid; s < S; s += kRsThreads) {
-    lru[s] = order[s];
-    tag_l[s] = tag[s];
-    flag[s] = 0;
+  // 0. loads: LRU order and slot tags (coalesced, then to LDS), hot pages;
+  //    this thread's selected tokens, then their page-table and reverse-map
+  //    entries
+  {
+    int ov[kRsSlots], tv[kRsSlots];
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (e < Q) {
+        const int x = min(e * kRsThreads + tid, S - 1);
+        ov[e] = order[x];
+        tv[e] = tag[x];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (e < Q) {
+        const int x = e * kRsThreads + tid;
+        lru[x] = x < S ? ov[e] : -1;
+        tag_l[x] = x < S ? tv[e] : -1;
+        flag[x] = 0;
+      }
+    }
   }
   for (int p = tid; p < HP; p += kRsThreads) hp[p] = hp_g[p];
-  for (int w = tid; w < sc.words; w += kRsThreads) st.mword[w] = 0ull;
+  for (int w = tid; w < 2 * sc.words; w += kRsThreads) st.mword[w] = 0u;
   if (tid == 0) st.n_res = st.n_hot = 0;
   int tok[kRsPos], code[kRsPos];  // code: pool row, -1 nothing, -2 miss
+  uint32_t missbits = 0u;  // bit e: position e of this thread is a miss
   int M, mbase;
   {
-    int g[kRsPos], slot[kRsPos];
+    int g[kRsPos], sl[kRsPos];
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
-      const int j = tid * P + e;
-      tok[e] = (e < P && j < K) ? sel[j] : -1;
+      if (e < P) {
+        const int j = tid * P + e;
+        const int t = sel[min(j, K - 1)];
+        tok[e] = j < K ? t : -1;
+      }
     }
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
-      const int t = tok[e];
-      const int tt = (t >= 0 && t < L) ? t : 0;  // in-range address either way
-      g[e] = pt[tt >> lps];
-      slot[e] = rev[tt];
+      if (e < P) {
+        const int t = tok[e];
+        const int tt = (t >= 0 && t < L) ? t : 0;  // an in-range address either way
+        g[e] = pt[tt >> lps];
+        sl[e] = rev[tt];
+      }
     }
     __syncthreads();  // LDS tables ready
     // 1. classify: resident > hot > miss (hit flags in LDS, no stores yet)
-    int nm = 0, nr = 0, nh = 0;
+    int hpg[kRsPos];
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
-      code[e] = -1;
-      const int j = tid * P + e;
-      const int t = tok[e];
-      if (!(e < P && j < K) || t < 0) continue;
-      if (t >= L) {
-        raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)t);
-      } else if (g[e] >= 0) {
-        code[e] = g[e] * ps + (t & (ps - 1));
-        ++nr;
-      } else if (slot[e] >= 0) {
-        const int sl = slot[e];
-        const int hpg = sl < S ? hp[sl >> lps] : -1;
-        if (hpg >= 0) {
-          flag[sl] = 1;
-          code[e] = hpg * ps + (sl & (ps - 1));
-          ++nh;
-        } else {
-          raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)sl);
-        }
-      } else {
-        code[e] = -2;
-        atomicOr(&st.mword[j >> 6], 1ull << (j & 63));
-        ++nm;
+      if (e < P) {
+        hpg[e] = hp[min(max(sl[e], 0), S - 1) >> lps];
       }
     }
+    int nm = 0, nr = 0, nh = 0;
+    int bad_tok = -1, bad_slot = -1;  // first offending entry of this thread
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P) {
+        const int j = tid * P + e;
+        const int t = tok[e];
+        const bool ok = t >= 0 && t < L;
+        const bool res = ok && g[e] >= 0;
+        const bool cand = ok && g[e] < 0 && sl[e] >= 0;
+        const bool hot = cand && sl[e] < S && hpg[e] >= 0;
+        const bool miss = ok && g[e] < 0 && sl[e] < 0;
+        bad_tok = (bad_tok < 0 && j < K && t >= L) ? t : bad_tok;
+        bad_slot = (bad_slot < 0 && cand && !hot) ? sl[e] : bad_slot;
+        if (hot) flag[sl[e]] = 1;
+        if (miss) atomicOr(&st.mword[j >> 5], 1u << (j & 31));
+        missbits |= miss ? (1u << e) : 0u;
+        code[e] = res ? g[e] * ps + (t & (ps - 1)) : hot ? hpg[e] * ps + (sl[e] & (ps - 1)) : miss ? -2 : -1;
+        nr += res ? 1 : 0;
+        nh += hot ? 1 : 0;
+        nm += miss ? 1 : 0;
+      }
+    }
+    if (bad_tok >= 0) raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)bad_tok);
+    if (bad_slot >= 0) raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)bad_slot);
     if (nr) atomicAdd(&st.n_res, nr);
     if (nh) atomicAdd(&st.n_hot, nh);
     mbase = block_excl_sum(nm, st.tmp, M);  // misses rank in token order
   }
-  // 2. untouched slots in LRU order; the first M of them are the victims
-  int my[kRsSlots];
-  int kc = 0;
+  // 2. untouched slots in LRU order (thread t holds LRU positions [tQ, tQ+Q));
+  //    the first M of them are the victims
+  int my[kRsSlots], ot[kRsSlots];
+  uint32_t km = 0u;  // bit e: my[e] is untouched
 #pragma unroll
-  for (int e = 0; e < kRsSlots; ++e) {
-    const int x = tid * Q + e;
-    const int s = (e < Q && x < S) ? lru[x] : -1;
-    my[e] = (s >= 0 && !(flag[s] & 1)) ? s : -1;
-    kc += my[e] >= 0 ? 1 : 0;
+  for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+    if (4 * e4 < Q) {
+      const int4 x = reinterpret_cast<const int4*>(lru + tid * Q)[e4];
+      my[4 * e4] = x.x;
+      my[4 * e4 + 1] = x.y;
+      my[4 * e4 + 2] = x.z;
+      my[4 * e4 + 3] = x.w;
+    }
+  }
+  {
+    int fl[kRsSlots];
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (e < Q) {
+        const int s = max(my[e], 0);
+        fl[e] = flag[s];
+        ot[e] = tag_l[s];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (e < Q) {
+        km |= (my[e] >= 0 && !(fl[e] & 1)) ? (1u << e) : 0u;
+      }
+    }
   }
   int kept;
-  const int kbase = block_excl_sum(kc, st.tmp, kept);  // (its barriers end the reads of lru)
+  const int kbase = block_excl_sum(__popc(km), st.tmp, kept);
+  // 3. victims (LDS)
   {
     int kpos = kbase;
 #pragma unroll
     for (int e = 0; e < kRsSlots; ++e) {
-      if (my[e] >= 0) {
-        if (kpos < M) {
-          vic[kpos] = my[e];
-          flag[my[e]] |= 2;
+      if (e < Q) {
+        if ((km >> e) & 1u) {
+          if (kpos < M) {
+            vic[kpos] = my[e];
+            flag[my[e]] |= 2;
+          }
+          ++kpos;
         }
-        ++kpos;
       }
     }
   }
   __syncthreads();
-  // 3. stores. New LRU order: the untouched non-victims in their order,
-  //    then the hit and victim slots in ascending slot number, which all
-  //    take stamp n. Victims lose their old token.
+  // fresh slots (hit or victim) of this thread's slot range [tQ, tQ + Q)
+  uint32_t fm = 0u;
+#pragma unroll
+  for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+    if (4 * e4 < Q) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(flag + tid * Q)[e4];
+      fm |= ((w & 0xFFu) ? 1u : 0u) << (4 * e4);
+      fm |= ((w & 0xFF00u) ? 1u : 0u) << (4 * e4 + 1);
+      fm |= ((w & 0xFF0000u) ? 1u : 0u) << (4 * e4 + 2);
+      fm |= ((w & 0xFF000000u) ? 1u : 0u) << (4 * e4 + 3);
+    }
+  }
+  int ftot;
+  const int fbase = (kept - M) + block_excl_sum(__popc(fm), st.tmp, ftot);
+  // the i-th miss takes the i-th victim
+  int vs[kRsPos];
+  {
+    int hv[kRsPos];
+    int mr = mbase;
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P) {
+        vs[e] = vic[min(mr, max(M - 1, 0))];
+        mr += code[e] == -2 ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P) hv[e] = hp[max(vs[e], 0) >> lps];
+    }
+    int bad_vic = -1;
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P && code[e] == -2) {
+        bad_vic = (bad_vic < 0 && hv[e] < 0) ? vs[e] : bad_vic;
+        code[e] = hv[e] >= 0 ? hv[e] * ps + (vs[e] & (ps - 1)) : -1;
+      }
+    }
+    if (bad_vic >= 0) raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)bad_vic);
+  }
+  // 4. plan and miss words, then the flag
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) {
+    const int j = tid * P + e;
+    if (e < P && j < K) put(&plan[j], code[e] >= 0 ? code[e] : -1);
+  }
+  for (int w = tid; w < sc.words; w += kRsThreads)
+    put_word(w, (unsigned long long)st.mword[2 * w] | ((unsigned long long)st.mword[2 * w + 1] << 32));
+  publish();
+  // 5. LRU state: the untouched non-victims keep their order at the front,
+  //    then the hit and victim slots in ascending slot number, all with
+  //    stamp n; victims lose their old token and take the missed one
   {
     int kpos = kbase;
 #pragma unroll
     for (int e = 0; e < kRsSlots; ++e) {
-      if (my[e] >= 0) {
-        if (kpos >= M) {
-          order[kpos - M] = my[e];
-        } else {
-          const int old = tag_l[my[e]];
-          if (old >= 0 && old < v.max_context) rev[old] = -1;
+      if (e < Q) {
+        if ((km >> e) & 1u) {
+          if (kpos >= M) {
+            order[kpos - M] = my[e];
+          } else if (ot[e] >= 0 && ot[e] < v.max_context) {
+            rev[ot[e]] = -1;
+          }
+          ++kpos;
         }
-        ++kpos;
+      }
+    }
+    int fpos = fbase;
+#pragma unroll
+    for (int e = 0; e < kRsSlots; ++e) {
+      if (e < Q && ((fm >> e) & 1u)) {
+        const int s = tid * Q + e;
+        order[fpos++] = s;
+        stamp[s] = n;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P && ((missbits >> e) & 1u)) {
+        tag[vs[e]] = tok[e];
+        rev[tok[e]] = vs[e];
       }
     }
   }
-  int fc = 0;
-#pragma unroll
-  for (int e = 0; e < kRsSlots; ++e) {
-    const int s = tid * Q + e;
-    fc += (e < Q && s < S && flag[s] != 0) ? 1 : 0;
-  }
-  int ftot;
-  int fpos = (kept - M) + block_excl_sum(fc, st.tmp, ftot);
-#pragma unroll
-  for (int e = 0; e < kRsSlots; ++e) {
-    const int s = tid * Q + e;
-    if (e < Q && s < S && flag[s] != 0) {
-      order[fpos++] = s;
-      stamp[s] = n;
-    }
-  }
-  // fill the victims with the misses (i-th miss -> i-th victim)
-  int mr = mbase;
-#pragma unroll
-  for (int e = 0; e < kRsPos; ++e) {
-    if (code[e] != -2) continue;
-    const int t = tok[e];
-    const int vs = vic[mr++];
-    tag[vs] = t;
-    rev[t] = vs;
-    const int hpg = hp[vs >> lps];
-    if (hpg >= 0) {
-      code[e] = hpg * ps + (vs & (ps - 1));
-    } else {
-      code[e] = -1;
-      raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)vs);
-    }
-  }
-  // 4. plan and miss words; publish them to the copy workgroups; counts
-#pragma unroll
-  for (int e = 0; e < kRsPos; ++e) {
-    const int j = tid * P + e;
-    if (e < P && j < K) plan[j] = code[e] < 0 ? -1 : code[e];
-  }
-  for (int w = tid; w < sc.words; w += kRsThreads) sc.miss_mask[(size_t)i * sc.words + w] = st.mword[w];
-  publish();
   if (tid == 0) {
     const int n_res = st.n_res, n_hot = st.n_hot;
     if (a.counts_out) {
@@ -332,9 +418,8 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) x[k][u] = s4[lane + 64 * u];
     }
   }
-  // wait for the bookkeeper: poll with plain device-coherent loads (an
-  // acquire per poll would invalidate the caches each time), one acquire
-  // fence once the flag is seen
+  // wait for the bookkeeper: poll with device-coherent loads; the plan and
+  // miss words it stored before raising the flag are read the same way
   if (tid == 0) {
     int spins = 0;
     while (__hip_atomic_load(&sc.flag[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
@@ -345,15 +430,19 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
     if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (!st.go) return;
   // (j0 is a multiple of 4, so the 4 bits lie in one mask word)
-  const unsigned am = (unsigned)((sc.miss_mask[(size_t)i * sc.words + (j0 >> 6)] >> (j0 & 63)) & 0xFull);
-  const int32_t* plan = a.plan_out + (size_t)i * K + j0;
+  const unsigned long long word = __hip_atomic_load(&sc.miss_mask[(size_t)i * sc.words + (j0 >> 6)],
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned am = (unsigned)((word >> (j0 & 63)) & 0xFull);
+  int32_t* plan = a.plan_out + (size_t)i * K + j0;
+  int dsts[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dsts[k] = ((am >> k) & 1u) ? __hip_atomic_load(&plan[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (!((am >> k) & 1u)) continue;
-    const int dst = plan[k];
+    const int dst = dsts[k];
     if (dst < 0) continue;
     u32x4* d4 = reinterpret_cast<u32x4*>(a.pool_rows + (int64_t)dst * ROW_BYTES);
     if ((gb >> k) & 1u) {
@@ -372,7 +461,7 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
     }
   }
   if (FP8 && lane < 4 && ((am >> lane) & 1u)) {  // one fp8 scale per missed row
-    const int dst = plan[lane];
+    const int dst = lane == 0 ? dsts[0] : lane == 1 ? dsts[1] : lane == 2 ? dsts[2] : dsts[3];
     if (dst >= 0) a.pool_scales[dst] = a.host_scales[hbase + t];
   }
 }
@@ -422,10 +511,10 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   sc.parts = (p->d.top_k + kRsPart - 1) / kRsPart;
   RsArgs a{idx, req_ids, n_req,
            pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
-           pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads),
+           max(4, pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads)),
            plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
            p->host_scales, p->pool_rows, p->pool_scales};
-  const size_t dyn = (rs_dyn_bytes(v.hot_rows, v.hot_pages_per_req) + 15) & ~(size_t)15;
+  const size_t dyn = (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req) + 15) & ~(size_t)15;
   const int grid = n_req * (1 + sc.parts);
   switch (p->d.kv_dtype) {
     case HS_F32:
