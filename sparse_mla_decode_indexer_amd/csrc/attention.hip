@@ -53,8 +53,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kAttThreads = 512;       // 8 waves
-constexpr int kQPerWG = 64;            // 4 blocks of 16 query rows
+// A workgroup takes QB blocks of 16 query rows with 2 waves per block
+// (launched with QB = 4).
 constexpr int kTile = 32;              // rows per tile
 constexpr int kChunks = 2 * kRowDim / 16;        // 72 chunks of 16 B per bf16 row
 constexpr int kRowChunks = kChunks + 1;          // LDS row stride: 73 chunks (one pad chunk)
@@ -120,8 +120,8 @@ __device__ inline float sum_across_kg(float x) {
 // LDS chunk position of 16-byte chunk c of tile row r.
 __device__ inline int swz(int r, int c) { return r * kRowChunks + c; }
 
-template <bool FP8>
-__global__ __launch_bounds__(kAttThreads) void k_attn_mfma(
+template <bool FP8, int QB>
+__global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     const uint16_t* __restrict__ q, int QR, const int32_t* __restrict__ plan, int K,
     const uint8_t* __restrict__ pool, const float* __restrict__ pool_scales, int64_t pool_rows_n,
     const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
@@ -135,12 +135,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attn_mfma(
   __shared__ __attribute__((aligned(16))) uint8_t wide[FP8 ? kTileBytes : 16];
   __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
   __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
-  __shared__ f32x4_t sbuf[2][4][2][64];  // partial scores [key half][q block][row block][lane]
+  __shared__ f32x4_t sbuf[2][QB][2][64];  // partial scores [key half][q block][row block][lane]
+  constexpr int kAttThreads = 128 * QB;
+  constexpr int kQPerWG = 16 * QB;
 
   const int sp = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, ln = lane & 15;
-  const int qb = wave & 3, half = wave >> 2;  // query block; key-dim half (QK) and value-dim half (PV)
+  const int qb = wave % QB, half = wave / QB;  // query block; key-dim half (QK) and value-dim half (PV)
   const int qh = hg * kQPerWG + qb * 16 + ln;
   const bool qvalid = qh < QR;
   const int32_t* pl = plan + (size_t)i * K;
@@ -473,14 +475,15 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
     return HS_OK;
   }
   const int n_tiles = (K + kTile - 1) / kTile;
-  const int n_hg = (QR + kQPerWG - 1) / kQPerWG;
   const uint8_t* zero_row = p->state + p->off.zero_row;
-  // Split the plan so that the grid covers the chip; a split is at least
-  // two tiles so that a workgroup's partial output stays below its row bytes.
-  // Split the plan so that about one workgroup per CU is busy; a split is at
-  // least 4 tiles so that the fixed cost per workgroup (plan, queries,
-  // partial output) is amortised.
+  constexpr int qb = 4;
+  const int q_per_wg = 16 * qb;
+  const int n_hg = (QR + q_per_wg - 1) / q_per_wg;
+  // Split the plan so that about one workgroup per CU is busy, with a floor
+  // on the tiles per split so that the fixed cost per workgroup (plan,
+  // queries, partial output) is amortised.
   static const int forced = env_int("HS_ATTN_TILES_PER_SPLIT", 0);
+  constexpr int min_tps = 4;
   int tps;
   if (forced > 0) {
     tps = forced;
@@ -488,7 +491,7 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
     const int base = n_req * n_hg;
     const int want = (256 + base - 1) / base;
     tps = (n_tiles + want - 1) / want;
-    if (tps < 4) tps = 4;
+    if (tps < min_tps) tps = min_tps;
   }
   if (tps > n_tiles) tps = n_tiles;
   if (tps > kAttMaxTilesPerSplit) tps = kAttMaxTilesPerSplit;
@@ -503,14 +506,16 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const float c2 = sm_scale * kLog2e;
   const dim3 grid(splits, n_hg, n_req);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  if (p->d.kv_dtype == HS_BF16)
-    k_attn_mfma<false><<<grid, kAttThreads, 0, s>>>(q16, QR, plan, K, p->pool_rows, nullptr, p->pool_rows_n,
-                                                    zero_row, c2, tps, splits, out, lse_out, part_o, part_lse,
-                                                    err);
+  const bool fp8 = p->d.kv_dtype != HS_BF16;
+  const float* sc = fp8 ? p->pool_scales : nullptr;
+#define HS_ATTN_LAUNCH(F, B)                                                                                  \
+  k_attn_mfma<F, B><<<grid, 128 * (B), 0, s>>>(q16, QR, plan, K, p->pool_rows, sc, p->pool_rows_n, zero_row, c2, \
+                                               tps, splits, out, lse_out, part_o, part_lse, err)
+  if (fp8)
+    HS_ATTN_LAUNCH(true, qb);
   else
-    k_attn_mfma<true><<<grid, kAttThreads, 0, s>>>(q16, QR, plan, K, p->pool_rows, p->pool_scales,
-                                                   p->pool_rows_n, zero_row, c2, tps, splits, out, lse_out,
-                                                   part_o, part_lse, err);
+    HS_ATTN_LAUNCH(false, qb);
+#undef HS_ATTN_LAUNCH
   if (splits > 1) {
     const int rows = n_req * QR;
     const int64_t threads = (int64_t)rows * (kNope / 4);
