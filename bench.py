@@ -10,11 +10,14 @@ steps are one hipGraph replay, bracketed by HIP events on the replay
 stream. Prints one JSON line.
 
 Roofline: the same K steps are replayed again from a snapshot of the
-pool state, with HIP events around each of the three entry points (a spin
-kernel first lets the host queue run ahead, so the events see GPU time
-only). The entry point with the largest average duration is reported
-against its bound (PCIe for the miss copy, HBM for the scans and gathers)
-with its algorithmic bytes per launch.
+pool state, with HIP events (on the stream the kernels run on) around each
+of the three entry points (a spin kernel first lets the host queue run
+ahead, so the events see GPU time only). The entry point with the largest
+average duration is reported against its bound (PCIe for the miss copy,
+HBM for the scans and gathers) with its algorithmic bytes per launch;
+`traffic` is the HBM bytes per launch its kernels actually moved, from the
+committed counter summary profiles/decode_step_<workload>_hbm_traffic.json
+(null when absent or taken on other kernel sources).
 
 cpu_baseline: the CPU oracle (tests' reference, fp64 numpy) timed on a
 bounded prefix of the same steps on this host.
@@ -46,11 +49,29 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "reference kernel that scales the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); requests are independent "
               "and shard by request with no exchange, so a multi-GPU figure is not measured here.",
@@ -164,9 +185,10 @@ def main():
         name = names[dom]
         d = per[name]
         achieved = d["bytes"] / (avg[dom] * 1e-6) / 1e9
-        roof = {"kernel": name, "bound": d["bound"], "achieved": round(achieved, 2),
-                "peak": d["peak"], "unit": "GB/s", "frac": round(achieved / d["peak"], 4),
-                "traffic": None,
+        roof = {"kernel": name, "kernels": ENTRY_KERNELS[name], "bound": d["bound"],
+                "achieved": round(achieved, 2), "peak": d["peak"], "unit": "GB/s",
+                "frac": round(achieved / d["peak"], 4),
+                "traffic": measured_traffic(spec.name, ENTRY_KERNELS[name]),
                 "avg_us": {n: round(float(a), 2) for n, a in zip(names, avg)},
                 "bytes_per_launch": {n: int(per[n]["bytes"]) for n in names},
                 "attention_tflops": round(flops_attn / (avg[2] * 1e-6) / 1e12, 2)}
@@ -206,6 +228,47 @@ def main():
     print(json.dumps(line))
 
 
+# HIP kernels behind each entry point (name prefixes as the profiler lists them)
+ENTRY_KERNELS = {
+    "select_topk": ["k_topk_filter", "k_topk_select"],
+    "resolve_rows": ["k_resolve"],
+    "sparse_mla_decode": ["k_attn_mfma", "k_attn_combine"],
+}
+
+
+def source_sha256() -> str:
+    """Hash of the kernel sources, as recorded with the HBM byte counters."""
+    import glob
+    import hashlib
+    src = sorted(glob.glob(os.path.join(ROOT, "sparse_mla_decode_indexer_amd", "csrc", "*")) +
+                 glob.glob(os.path.join(ROOT, "include", "*.h")))
+    h = hashlib.sha256()
+    for p in src:
+        h.update(os.path.relpath(p, ROOT).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernels):
+    """HBM bytes per launch of an entry point from the committed counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a plain copy), or None when
+    there is none for this workload or the kernel sources have changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_sha256():
+        return None
+    total = 0
+    for name, k in t["kernels"].items():
+        if any(name.startswith(p) for p in kernels):
+            total += int(k["hbm_bytes"])
+    return total or None
+
+
 def cpu_baseline(wl, host_scores, host_q, sched, budget_s):
     """Time the CPU oracle (full step: top-K, LRU, fp64 attention) on the
     first steps of the same inputs until the budget is spent."""
@@ -218,16 +281,23 @@ def cpu_baseline(wl, host_scores, host_q, sched, budget_s):
                        sm_scale=wl.sm_scale)
     t0 = time.perf_counter()
     n = 0
-    while n < len(host_scores) and time.perf_counter() - t0 < budget_s:
-        q = host_q[n]
+    m = len(host_scores)
+    while time.perf_counter() - t0 < budget_s:  # cycles through the stored steps
+        j = n % m
+        q = host_q[j]
         qd = bf16_decode(q) if q.dtype == np.uint16 else q.astype(np.float64)
-        orc.step(host_scores[n], qd, sched[n], with_attention=True)
+        orc.step(host_scores[j], qd, sched[j], with_attention=True)
         n += 1
     el = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
+    try:  # the BLAS threads numpy actually runs with
+        from threadpoolctl import threadpool_info
+        cores = max([int(x["num_threads"]) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
     return {"value": round(n / el, 3), "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} decode steps of {s.name} (top-K sort, LRU simulation, fp64 "
-                      f"attention over all heads), numpy with up to {cores} BLAS threads",
+            "sample": f"{n} decode steps of {s.name} (its first {min(n, m)} score/query sets, "
+                      f"repeated; top-K sort, LRU simulation, fp64 attention over all heads), "
+                      f"numpy with {cores} BLAS threads, {el:.1f} s",
             "seconds": round(el, 2)}
 
 
