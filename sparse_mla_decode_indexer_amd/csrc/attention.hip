@@ -363,29 +363,23 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.f;
   if (M != -INFINITY) {
-    int s = 0;
-    for (; s + 4 <= n_splits; s += 4) {
-      float w[4];
-      float4 x[4];
+    constexpr int kBatch = 16;  // partial loads in flight per thread
+    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+      float w[kBatch];
+      float4 x[kBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t pr = base + (size_t)(s + u) * QR;
-        w[u] = part_lse[pr];
+      for (int u = 0; u < kBatch; ++u) {
+        const int s = min(s0 + u, n_splits - 1);
+        const size_t pr = base + (size_t)s * QR;
+        w[u] = s0 + u < n_splits ? part_lse[pr] : -INFINITY;
         x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float e = __builtin_amdgcn_exp2f(w[u] - M);
+      for (int u = 0; u < kBatch; ++u) {
+        const float e = __builtin_amdgcn_exp2f(w[u] - M);  // 0 for the padding entries
         W += e;
         o.x += e * x[u].x; o.y += e * x[u].y; o.z += e * x[u].z; o.w += e * x[u].w;
       }
-    }
-    for (; s < n_splits; ++s) {
-      const size_t pr = base + (size_t)s * QR;
-      const float e = __builtin_amdgcn_exp2f(part_lse[pr] - M);
-      const float4 x = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
-      W += e;
-      o.x += e * x.x; o.y += e * x.y; o.z += e * x.z; o.w += e * x.w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
