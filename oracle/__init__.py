@@ -15,7 +15,8 @@ Pages it follows (cited by title and section):
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (brute force, closed forms, library routines, a hand-computed
 LRU trace, invariants). Conventions the pages leave open — the softmax scale
-value, the choice of the first 512 dims as V, and the LRU tie rules — are
+value, the choice of the first 512 dims as V, the LRU tie rules and the
+page-coldness order of the residency manager — are
 fixed here and shared with the HIP path; the pages cannot confirm them
 ("parity unpinned" by the pages; pinned only as conventions).
 """
@@ -30,3 +31,4 @@ from .hisparse_oracle import (  # noqa: F401
     resolve_step,
     select_topk,
 )
+from .residency import PageState, update_residency  # noqa: F401

@@ -34,6 +34,8 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
+from .residency import PageState, update_residency
+
 RESIDENT, HOT, MISS = 0, 1, 2
 NOPE = 512
 
@@ -219,6 +221,21 @@ class DecodeOracle:
         self.ps, self.K = int(page_size), int(top_k)
         self.sm_scale = float(np.float32(sm_scale))
         self.hot = [HotBufferOracle(hot_rows, c) for c in ctx_capacity]
+        # page recency and host-copy marks for the residency manager
+        self.pages = [PageState(len(g)) for g in self.gpu_page]
+        for r, g in enumerate(self.gpu_page):
+            self.pages[r].mark_given(0, g, host_copy_valid=False)
+        self.prev_len = [0] * len(self.gpu_page)
+
+    def set_pages(self, r: int, first_page: int, gpu_ids: np.ndarray, host_copy_valid: bool = False):
+        """Residency of pages [first_page, first_page + len) set from outside."""
+        g = np.asarray(gpu_ids, dtype=np.int64)
+        self.gpu_page[r][first_page:first_page + g.size] = g
+        self.pages[r].mark_given(first_page, g, host_copy_valid)
+
+    def update_residency(self, r: int, budget: Optional[int], max_copy: int, max_demote: int):
+        return update_residency(self.pages[r], self.gpu_page[r], self.prev_len[r], self.ps,
+                                budget, max_copy, max_demote)
 
     def logical_rows(self, r: int, tokens: np.ndarray) -> np.ndarray:
         idx = self.host_base[r] + tokens
@@ -233,8 +250,12 @@ class DecodeOracle:
         out = {"idx": [], "plan": [], "kind": [], "counts": [], "miss_tokens": [],
                "miss_slots": [], "out": [], "lse": []}
         for r in range(R):
+            # pages entering the context take the step count before this resolve
+            self.pages[r].enter_context(self.prev_len[r], int(lens[r]), self.hot[r].step, self.ps)
+            self.prev_len[r] = int(lens[r])
             sel = select_topk(scores[r], int(lens[r]), self.K)
             res = resolve_step(self.hot[r], sel, self.gpu_page[r], self.hot_pages[r], self.ps)
+            self.pages[r].touch(sel, self.hot[r].step, self.ps)
             out["idx"].append(sel)
             for k in ("plan", "kind", "counts", "miss_tokens", "miss_slots"):
                 out[k].append(res[k])
