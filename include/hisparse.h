@@ -11,6 +11,9 @@
  *                       copy that single row from pinned host memory into
  *                       the least-recently-used hot slot;
  *   hs_sparse_mla_decode absorbed-MLA decode attention over only those rows.
+ * Around the step, hs_update_residency copies completed GPU pages to the
+ * host store ahead of need and, under a GPU page budget, moves a request's
+ * coldest pages back to host memory.
  *
  * Pages describing the method (cited by title and section):
  *   [P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" (agentlenshq.com)
@@ -76,7 +79,11 @@ enum {
 };
 
 /* hs_set_residency flags */
-enum { HS_RESET_HOT = 1u /* empty the request's hot buffer (nothing hot) */ };
+enum {
+  HS_RESET_HOT = 1u,        /* empty the request's hot buffer (nothing hot) */
+  HS_HOST_COPY_VALID = 2u,  /* the host store already holds the rows of the GPU pages given */
+  HS_RESET_PAGES = 4u       /* a new request: page stamps and host-copy marks start from zero */
+};
 
 /*
  * Pool description. The latent row layout is MLA's: nope_dim (512) dims that
@@ -129,6 +136,11 @@ typedef struct hs_state_layout {
   size_t step;        /* int32 [max_requests]: resolves done so far */
   size_t counters;    /* int64 [max_requests][3]: cumulative resident, hot, miss */
   size_t error;       /* uint32 [4]: code, request, index, 0 */
+  size_t page_stamp;  /* int32 [max_requests][pages_per_request]: last step whose top-K
+                         selected a token of the page, or the step at which the page
+                         entered the context; 0 = neither */
+  size_t host_valid;  /* uint8 [max_requests][pages_per_request]: 1 when the host store
+                         holds the page's rows (always for host-only pages) */
   size_t scratch;     /* start of internal scratch */
   size_t total;       /* == hs_pool_sizes.state_bytes */
 } hs_state_layout;
@@ -172,7 +184,14 @@ hs_status hs_host_rows(hs_pool* pool, void** rows, float** scales);
  *                  request's hot buffer, or NULL to keep the current lease
  *                  (must be given once before the first resolve)
  *   flags          HS_RESET_HOT empties the hot buffer ([P2] state 3: a
- *                  request that starts host-only loads rows only on demand)
+ *                  request that starts host-only loads rows only on demand);
+ *                  HS_HOST_COPY_VALID: the host store already holds the rows
+ *                  of the GPU pages given here (else they count as not yet
+ *                  copied; host-only pages always hold a host copy);
+ *                  HS_RESET_PAGES: clear the request's page stamps and
+ *                  host-copy marks first (a new request in this slot)
+ * Pages that enter the context (from ceil(old L / page_size) up to
+ * ceil(L_r / page_size)) take the request's current step as page stamp.
  * No hot invalidation is needed when pages move: a page that is back on GPU
  * is read in place before any stale hot copy. Errors: INVALID_ARGUMENT. */
 hs_status hs_set_residency(hs_pool* pool, int32_t req, int32_t context_len,
@@ -235,6 +254,37 @@ hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype,
                                int32_t n_req, int32_t q_per_req, int32_t n_heads,
                                const int32_t* plan, float sm_scale, float* out,
                                float* lse_out, hipStream_t stream);
+
+/* Residency manager ([P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载"
+ * §"混合 HiSparse 的技术实现": fully resident requests have their completed
+ * prefix pages copied to host memory ahead of need, hybrid requests keep
+ * the tail on GPU and older pages on host; §"关键架构细节", proactive copy:
+ * the copies let GPU pages be released at once under pressure; [P3]
+ * §"分级内存的运作机制": under memory pressure a request releases its
+ * coldest pages to host memory). For each i < n_req, request r = req_ids[i]:
+ *   1. proactive copy: of the GPU pages entirely inside the context that
+ *      have no host copy, the lowest-numbered max_copy_pages are copied
+ *      (rows, and fp8 scales) from the pool into the host store over PCIe
+ *      and marked host-valid;
+ *   2. demotion: while the request holds more GPU pages (pages below
+ *      ceil(L_r / page_size) with a pool page) than budget_pages[i], its
+ *      coldest demotable pages leave the GPU (page table -1), at most
+ *      max_demote_pages per call. Demotable: entirely inside the context
+ *      and host-valid (after step 1). Coldest: ascending (page stamp, page)
+ *      (page stamps: hs_state_layout).
+ *   budget_pages    device int32 [n_req], >= 0; NULL = no demotion
+ *   freed_out       device int32 [n_req][max_demote_pages]: pool pages given
+ *                   back, in ascending logical page order, -1 padded (the
+ *                   caller owns pool pages and may reuse them); NULL only
+ *                   when max_demote_pages = 0
+ *   counts_out      device int32 [n_req][2]: pages copied, pages demoted;
+ *                   may be NULL
+ * max_copy_pages, max_demote_pages: 0 .. 1024. Graph-capturable.
+ * Errors: INVALID_ARGUMENT, CAPACITY (n_req > max_batch). */
+hs_status hs_update_residency(hs_pool* pool, const int32_t* req_ids, int32_t n_req,
+                              const int32_t* budget_pages, int32_t max_copy_pages,
+                              int32_t max_demote_pages, int32_t* freed_out, int32_t* counts_out,
+                              hipStream_t stream);
 
 /* Byte offsets of the state arrays in the workspace. Errors: INVALID_ARGUMENT. */
 hs_status hs_get_state_layout(const hs_pool* pool, hs_state_layout* out);

@@ -17,6 +17,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
 HS_RESET_HOT = 1
+HS_HOST_COPY_VALID = 2
+HS_RESET_PAGES = 4
 DTYPE_CODES = {"f32": HS_F32, "bf16": HS_BF16, "fp8": HS_FP8_E4M3}
 STATUS = {0: "HS_OK", 1: "HS_ERR_INVALID_ARGUMENT", 2: "HS_ERR_CAPACITY", 3: "HS_ERR_UNSUPPORTED",
           4: "HS_ERR_HIP", 5: "HS_ERR_OUT_OF_MEMORY", 6: "HS_ERR_DEVICE"}
@@ -44,7 +46,7 @@ class HsPoolSizes(ctypes.Structure):
 class HsStateLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "ctx_len", "host_base", "page_table", "hot_pages", "rev", "slot_tag", "slot_stamp",
-        "lru_order", "step", "counters", "error", "scratch", "total")]
+        "lru_order", "step", "counters", "error", "page_stamp", "host_valid", "scratch", "total")]
 
 
 class HiSparseError(RuntimeError):
@@ -61,6 +63,7 @@ _SIGS = {
     "hs_set_residency": [_VP, _I32, _I32, _I64, _I32, _I32, _VP, _VP, _U32, _VP],
     "hs_select_topk": [_VP, _VP, _I64, _VP, _I32, _VP, _VP],
     "hs_resolve_rows": [_VP, _VP, _VP, _I32, _VP, _VP, _VP],
+    "hs_update_residency": [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _VP],
     "hs_sparse_mla_decode": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
     "hs_get_state_layout": [_VP, ctypes.POINTER(HsStateLayout)],
     "hs_get_device_error": [_VP, ctypes.POINTER(_U32 * 4), _VP],
@@ -144,6 +147,13 @@ def resolve_rows(pool: int, idx: int, req_ids: int, n_req: int, plan_out: int, c
                  stream: int):
     _check(lib().hs_resolve_rows(pool, idx, req_ids, n_req, plan_out, counts_out or None, stream or None),
            "hs_resolve_rows")
+
+
+def update_residency(pool: int, req_ids: int, n_req: int, budget_pages: int, max_copy_pages: int,
+                     max_demote_pages: int, freed_out: int, counts_out: int, stream: int):
+    _check(lib().hs_update_residency(pool, req_ids, n_req, budget_pages or None, max_copy_pages,
+                                     max_demote_pages, freed_out or None, counts_out or None,
+                                     stream or None), "hs_update_residency")
 
 
 def sparse_mla_decode(pool: int, q: int, q_dtype: int, n_req: int, q_per_req: int, n_heads: int,

@@ -25,6 +25,10 @@ constexpr int kTkStage = 8192;     // survivors staged in LDS by the select work
 // resolve
 constexpr int kRsThreads = 1024;
 
+// residency manager
+constexpr int kRuThreads = 1024;
+constexpr int kRuMaxList = 1024;   // most pages copied or demoted per call
+
 // attention
 constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)
 constexpr int kAttMinPartRows = 16384;  // at least this many partial rows (32 MiB)
@@ -71,6 +75,8 @@ struct StateView {
   int32_t* step;
   int64_t* counters;
   uint32_t* error;
+  int32_t* page_stamp;
+  uint8_t* host_valid;
   int32_t max_requests, max_context, pages_per_req, hot_rows, hot_pages_per_req;
   int32_t page_size, log2_ps, num_pool_pages, top_k;
 };
@@ -88,6 +94,9 @@ hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int
                       int32_t n_req, int32_t* idx_out, hipStream_t s);
 hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
                          int32_t* plan_out, int32_t* counts_out, hipStream_t s);
+hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_req,
+                                  const int32_t* budget, int32_t max_copy, int32_t max_demote,
+                                  int32_t* freed_out, int32_t* counts_out, hipStream_t s);
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
                            int32_t q_per_req, int32_t n_heads, const int32_t* plan,
                            float sm_scale, float* out, float* lse_out, hipStream_t s);

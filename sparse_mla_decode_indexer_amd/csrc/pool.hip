@@ -79,6 +79,8 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   L.step = take(4 * R);
   L.counters = take(8 * 3 * R);
   L.error = take(16);
+  L.page_stamp = take(4 * R * ppr);
+  L.host_valid = take(R * ppr);
   L.scratch = o;
   Offsets of{};
   of.zero_row = take(4 * kRowDim);
@@ -116,6 +118,8 @@ StateView make_view(const hs_pool* p) {
   v.step = reinterpret_cast<int32_t*>(s + p->lay.step);
   v.counters = reinterpret_cast<int64_t*>(s + p->lay.counters);
   v.error = reinterpret_cast<uint32_t*>(s + p->lay.error);
+  v.page_stamp = reinterpret_cast<int32_t*>(s + p->lay.page_stamp);
+  v.host_valid = s + p->lay.host_valid;
   v.max_requests = p->d.max_requests;
   v.max_context = p->d.max_context;
   v.pages_per_req = p->sz.pages_per_request;
@@ -149,10 +153,27 @@ __global__ void k_set_residency(StateView v, int32_t req, int32_t ctx, int64_t b
                                 const int32_t* __restrict__ gpu_pages,
                                 const int32_t* __restrict__ hot_page_ids, uint32_t flags) {
   const int tid = threadIdx.x;
+  const int ps = v.page_size;
+  int32_t* stamp = v.page_stamp + (size_t)req * v.pages_per_req;
+  uint8_t* hv = v.host_valid + (size_t)req * v.pages_per_req;
+  const bool fresh = (flags & HS_RESET_PAGES) != 0;
+  const int old_pages = fresh ? 0 : (v.ctx_len[req] + ps - 1) / ps;
+  const int new_pages = (ctx + ps - 1) / ps;
+  const int n = v.step[req];
+  __syncthreads();  // every thread has read the old context length
   if (tid == 0) {
     v.ctx_len[req] = ctx;
     v.host_base[req] = base;
   }
+  if (fresh) {
+    for (int p = tid; p < v.pages_per_req; p += blockDim.x) {
+      stamp[p] = 0;
+      hv[p] = 0;
+    }
+    __syncthreads();
+  }
+  // pages entering the context take the current step as their stamp
+  for (int p = old_pages + tid; p < new_pages; p += blockDim.x) stamp[p] = n;
   int32_t* pt = v.page_table + (size_t)req * v.pages_per_req;
   for (int i = tid; i < num_pages; i += blockDim.x) {
     int32_t g = gpu_pages[i];
@@ -161,6 +182,7 @@ __global__ void k_set_residency(StateView v, int32_t req, int32_t ctx, int64_t b
       g = -1;
     }
     pt[first_page + i] = g;
+    hv[first_page + i] = (g < 0 || (flags & HS_HOST_COPY_VALID)) ? 1 : 0;
   }
   if (hot_page_ids) {
     int32_t* hp = v.hot_pages + (size_t)req * v.hot_pages_per_req;
@@ -294,11 +316,25 @@ hs_status hs_set_residency(hs_pool* pool, int32_t req, int32_t context_len, int6
   if (first_page < 0 || num_pages < 0 || first_page + num_pages > pool->sz.pages_per_request)
     return HS_ERR_INVALID_ARGUMENT;
   if (num_pages > 0 && !gpu_page_ids) return HS_ERR_INVALID_ARGUMENT;
-  if (flags & ~(uint32_t)HS_RESET_HOT) return HS_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(HS_RESET_HOT | HS_HOST_COPY_VALID | HS_RESET_PAGES)) return HS_ERR_INVALID_ARGUMENT;
   k_set_residency<<<1, 1024, 0, stream>>>(make_view(pool), req, context_len, host_row_base,
                                           first_page, num_pages, gpu_page_ids, hot_page_ids, flags);
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
+}
+
+hs_status hs_update_residency(hs_pool* pool, const int32_t* req_ids, int32_t n_req,
+                              const int32_t* budget_pages, int32_t max_copy_pages,
+                              int32_t max_demote_pages, int32_t* freed_out, int32_t* counts_out,
+                              hipStream_t stream) {
+  if (!pool || !req_ids || n_req < 0) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch) return HS_ERR_CAPACITY;
+  if (max_copy_pages < 0 || max_copy_pages > kRuMaxList) return HS_ERR_INVALID_ARGUMENT;
+  if (max_demote_pages < 0 || max_demote_pages > kRuMaxList) return HS_ERR_INVALID_ARGUMENT;
+  if (max_demote_pages > 0 && !freed_out) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req == 0) return HS_OK;
+  return launch_update_residency(pool, req_ids, n_req, budget_pages, max_copy_pages, max_demote_pages,
+                                 freed_out, counts_out, stream);
 }
 
 hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_stride,

@@ -359,6 +359,13 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
         rev[tok[e]] = vs[e];
       }
     }
+    // page recency for the residency manager: every page the indexer
+    // selected a token of this step takes stamp n
+    int32_t* pstamp = v.page_stamp + (size_t)r * v.pages_per_req;
+#pragma unroll
+    for (int e = 0; e < kRsPos; ++e) {
+      if (e < P && tok[e] >= 0 && tok[e] < L) pstamp[tok[e] >> lps] = n;
+    }
   }
   if (tid == 0) {
     const int n_res = st.n_res, n_hot = st.n_hot;

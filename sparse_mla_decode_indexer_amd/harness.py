@@ -74,12 +74,17 @@ def load_workload(pool: TieredPool, wl: W.Workload, poison_hot: bool = True,
 
 
 def set_request(pool: TieredPool, wl: W.Workload, r: int, ctx: int, reset_hot: bool = False,
-                with_hot_pages: bool = False, gpu_page: Optional[np.ndarray] = None):
+                with_hot_pages: bool = False, gpu_page: Optional[np.ndarray] = None,
+                first_page: int = 0, num_pages: Optional[int] = None):
+    """Context length of request r, and the residency of pages
+    [first_page, first_page + num_pages) (default: every page of the
+    workload's table) from `gpu_page` (default: the workload's)."""
     dev = pool.device
     g = wl.gpu_page[r] if gpu_page is None else gpu_page
-    gp = torch.from_numpy(g.astype(np.int32)).to(dev)
+    n = g.size - first_page if num_pages is None else num_pages
+    gp = torch.from_numpy(g[first_page:first_page + n].astype(np.int32)).to(dev) if n > 0 else None
     hp = torch.from_numpy(wl.hot_pages[r].astype(np.int32)).to(dev) if with_hot_pages else None
-    pool.set_residency(r, ctx, int(wl.host_base[r]), gp, 0, hp, reset_hot)
+    pool.set_residency(r, ctx, int(wl.host_base[r]), gp, first_page, hp, reset_hot)
 
 
 class StepBuffers:

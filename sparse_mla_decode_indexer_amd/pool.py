@@ -80,16 +80,27 @@ class TieredPool:
             "step": v(L.step, torch.int32, R),
             "counters": v(L.counters, torch.int64, R, 3),
             "error": v(L.error, torch.int32, 4),
+            "page_stamp": v(L.page_stamp, torch.int32, R, self.pages_per_request),
+            "host_valid": v(L.host_valid, torch.uint8, R, self.pages_per_request),
         }
 
     # ------------------------------------------------------------ calls
     def set_residency(self, req: int, context_len: int, host_row_base: int,
                       gpu_page_ids: Optional[torch.Tensor], first_page: int = 0,
-                      hot_page_ids: Optional[torch.Tensor] = None, reset_hot: bool = False):
+                      hot_page_ids: Optional[torch.Tensor] = None, reset_hot: bool = False,
+                      host_copy_valid: bool = False, reset_pages: bool = False):
         n = 0 if gpu_page_ids is None else int(gpu_page_ids.numel())
+        flags = ((B.HS_RESET_HOT if reset_hot else 0) | (B.HS_HOST_COPY_VALID if host_copy_valid else 0) |
+                 (B.HS_RESET_PAGES if reset_pages else 0))
         B.set_residency(self.handle, req, context_len, host_row_base, first_page, n,
-                        _ptr(gpu_page_ids), _ptr(hot_page_ids), B.HS_RESET_HOT if reset_hot else 0,
-                        _stream())
+                        _ptr(gpu_page_ids), _ptr(hot_page_ids), flags, _stream())
+
+    def update_residency(self, req_ids: torch.Tensor, budget_pages: Optional[torch.Tensor],
+                         max_copy_pages: int, max_demote_pages: int,
+                         freed_out: Optional[torch.Tensor] = None,
+                         counts_out: Optional[torch.Tensor] = None):
+        B.update_residency(self.handle, req_ids.data_ptr(), int(req_ids.numel()), _ptr(budget_pages),
+                           max_copy_pages, max_demote_pages, _ptr(freed_out), _ptr(counts_out), _stream())
 
     def select_topk(self, scores: torch.Tensor, req_ids: torch.Tensor, idx_out: torch.Tensor):
         B.select_topk(self.handle, scores.data_ptr(), scores.stride(0), req_ids.data_ptr(),

@@ -69,6 +69,8 @@ class Runner:
         self.n = 0
         self.raw = Hn.store_bytes(wl)
         self.max_err = 0.0
+        self.incremental = False          # growth sets only the new pages
+        self.cur_len = np.asarray(wl.ctx0).copy()
 
     def step(self, heads: Optional[Sequence[int]] = None, graph: bool = False):
         """Run one step on GPU and oracle and compare. `heads` restricts the
@@ -77,7 +79,13 @@ class Runner:
         lens = self.sched[self.n]
         if s.growth is not None:
             for r in range(s.n_req):
-                Hn.set_request(self.pool, wl, r, int(lens[r]))
+                if self.incremental:  # only the pages entering the context
+                    ps = s.page_size
+                    a_, b_ = -(-int(self.cur_len[r]) // ps), -(-int(lens[r]) // ps)
+                    Hn.set_request(self.pool, wl, r, int(lens[r]), first_page=a_, num_pages=b_ - a_)
+                else:
+                    Hn.set_request(self.pool, wl, r, int(lens[r]))
+        self.cur_len = np.asarray(lens).copy()
         sc = self.scores.next(lens)
         q = self.queries.next()
         self.buf.upload(0, sc, q)
@@ -131,6 +139,11 @@ class Runner:
             slots = np.arange(hb.S)
             assert np.array_equal(st["lru_order"][r], np.lexsort((slots, hb.stamp))), f"{tag} req {r}: LRU order"
             assert st["step"][r] == hb.step
+            pg = self.oracle.pages[r]
+            n = pg.stamp.size
+            assert np.array_equal(st["page_stamp"][r][:n], pg.stamp), f"{tag} req {r}: page stamps"
+            assert np.array_equal(st["host_valid"][r][:n].astype(bool), pg.host_valid), f"{tag} req {r}: host copies"
+            assert np.array_equal(st["page_table"][r][:n], self.oracle.gpu_page[r]), f"{tag} req {r}: page table"
 
     def _check_rows(self, idx, plan, tag: str):
         prv = self.pool.pool_row_view()
