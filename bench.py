@@ -193,6 +193,8 @@ def main():
                 "bytes_per_launch": {n: int(per[n]["bytes"]) for n in names},
                 "attention_tflops": round(flops_attn / (avg[2] * 1e-6) / 1e12, 2)}
 
+    resid = None if args.no_roofline else residency_probe(pool, buf, spec)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, host_scores, host_q, sched, args.cpu_seconds)
@@ -223,6 +225,7 @@ def main():
         "step_pcie_frac": round(b_pcie / (ms_per_step * 1e-3) / 1e9 / PCIE_PEAK_GBS, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "residency_manager": resid,
     }
     pool.close()
     print(json.dumps(line))
@@ -267,6 +270,45 @@ def measured_traffic(workload: str, kernels):
         if any(name.startswith(p) for p in kernels):
             total += int(k["hbm_bytes"])
     return total or None
+
+
+def residency_probe(pool, buf, spec, pages_per_call: int = 64, calls: int = 4):
+    """Residency manager on the benchmark's pool after the timed steps (not
+    part of a decode step): proactive copies of `pages_per_call` complete GPU
+    pages per call into the pinned host store (PCIe device-to-host writes),
+    then one release call under a budget of half the GPU pages. HIP events on
+    the stream the kernel runs on."""
+    import torch
+    R = spec.n_req
+    dev = buf.req_ids.device
+    counts = torch.zeros(R, 2, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    copy_ms, copied = 0.0, 0
+    for _ in range(calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pool.update_residency(buf.req_ids, None, pages_per_call, 0, None, counts)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms += e0.elapsed_time(e1)
+        copied += int(counts[:, 0].sum().item())
+    pt = pool.state_views()["page_table"]
+    held = int((pt[:R] >= 0).sum().item())
+    budget = torch.full((R,), max(held // (2 * R), 0), dtype=torch.int32, device=dev)
+    freed = torch.empty(R, 1024, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    pool.update_residency(buf.req_ids, budget, 0, 1024, freed, counts)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    released = int(counts[:, 1].sum().item())
+    row_bytes = pool.row_bytes + (4 if spec.kv_dtype == "fp8" else 0)
+    copied_bytes = copied * spec.page_size * row_bytes
+    gbs = copied_bytes / (copy_ms * 1e-3) / 1e9 if copied else 0.0
+    return {"calls": calls, "copied_pages": copied, "copied_bytes": copied_bytes,
+            "copy_call_us": round(copy_ms * 1e3 / calls, 2), "copy_gbs": round(gbs, 2),
+            "pcie_peak_gbs": PCIE_PEAK_GBS, "copy_frac": round(gbs / PCIE_PEAK_GBS, 4),
+            "release_call_us": round(e0.elapsed_time(e1) * 1e3, 2), "released_pages": released}
 
 
 def cpu_baseline(wl, host_scores, host_q, sched, budget_s):
