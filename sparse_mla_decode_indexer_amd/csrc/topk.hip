@@ -204,6 +204,7 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   constexpr int NW = kTkSelWaves;
   __shared__ __align__(16) uint32_t hist[3][kTkBins];
   __shared__ int off[kTkMaxChunks + 1];
+  __shared__ int off2[kTkMaxChunks + 1];
   __shared__ uint2 surv[kTkStage];
   __shared__ int wtot[NW];
   __shared__ int weq[NW];
@@ -252,9 +253,105 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   for (int w = 0; w < NW; ++w) kmax = max(kmax, wmax[w]);
   const int total = run;
   const bool raw = total < K;  // fewer than K passed: select over the raw scores
-  const bool staged = !raw && total <= kTkStage;
-  const int n = raw ? L : total;
-  const uint32_t base = raw ? 0u : thr;
+  bool staged = !raw && total <= kTkStage;
+  bool narrowed = false;
+  int n = raw ? L : total;
+  uint32_t base = raw ? 0u : thr;
+
+  // Too many survivors for LDS (e.g. the first call, bound 0): find a cut
+  // key, the lower edge of a digit bin of (key - bound), with K <= #{key >=
+  // cut} <= kTkStage by histogram passes that read the chunk slices in
+  // order (coalesced, UN loads in flight per lane), then stage the survivors
+  // >= cut in token order. nb0 is the lower edge of the first pass's bin
+  // holding rank 5K/4, the next call's bound when fewer than 5K/4 are staged.
+  uint32_t nb0 = thr;
+  if (!raw && !staged) {
+    constexpr int UN = 8;
+    // f(u, key, valid) for every slot of this wave's chunks, all lanes together
+    auto sweep = [&](auto&& f, auto&& chunk_begin, auto&& chunk_end) {
+      for (int c = wave; c < nch; c += NW) {
+        const int m = off[c + 1] - off[c];
+        const uint2* src = cand + (size_t)c * kTkChunk;
+        chunk_begin(c);
+        for (int j0 = 0; j0 < m; j0 += 64 * UN) {
+          uint2 e[UN];
+#pragma unroll
+          for (int u = 0; u < UN; ++u) {
+            const int j = j0 + 64 * u + lane;
+            e[u] = j < m ? src[j] : make_uint2(0u, 0u);
+          }
+#pragma unroll
+          for (int u = 0; u < UN; ++u) f(e[u], j0 + 64 * u + lane < m);
+        }
+        chunk_end(c);
+      }
+    };
+    auto none = [](int) {};
+    const uint32_t range0 = kmax - thr;
+    const int B0 = range0 == 0u ? 0 : 32 - __clz(range0);
+    int shc = B0 > 12 ? B0 - 12 : 0;  // shift of the digit found last
+    uint32_t pre = 0u;                // digits found so far
+    int above = 0, cnt_ge = n;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int w = pass == 0 ? 0 : min(12, shc);
+      const int sn = shc - w;
+      if (pass > 0 && (cnt_ge <= kTkStage || shc == 0)) break;  // uniform
+      uint32_t* h = hist[pass];
+      const uint32_t dmask = (1u << w) - 1u;
+      sweep([&](uint2 e, bool ok) {
+        const uint32_t rel = e.x - thr;
+        if (ok && pass == 0) atomicAdd(&h[rel >> shc], 1u);
+        if (ok && pass > 0 && (rel >> shc) == pre) atomicAdd(&h[(rel >> sn) & dmask], 1u);
+      }, none, none);
+      __syncthreads();
+      FindOut g;
+      hist_find2(h, K - above, pass == 0 ? min(n, K + K / 4) : K - above, wtot, &fres, g);
+      if (pass == 0) nb0 = thr + ((uint32_t)g.b[1] << shc);
+      cnt_ge = above + g.above[0] + (int)h[g.b[0]];
+      pre = pass == 0 ? (uint32_t)g.b[0] : ((pre << w) | (uint32_t)g.b[0]);
+      above += g.above[0];
+      if (pass > 0) shc = sn;
+      __syncthreads();  // h is read above by every thread
+    }
+    if (cnt_ge <= kTkStage) {
+      const uint32_t cut = thr + (pre << shc);
+      // survivors >= cut per chunk, then their offsets
+      int k = 0;
+      sweep([&](uint2 e, bool ok) { k += __popcll(__ballot(ok && e.x >= cut)); }, [&](int) { k = 0; },
+            [&](int c) {
+              if (lane == 0) off2[c] = k;
+            });
+      __syncthreads();
+      int run2 = 0;
+      for (int b0 = 0; b0 < nch; b0 += kTkSelThreads) {
+        const int cc = b0 + tid;
+        const int x = cc < nch ? off2[cc] : 0;
+        int tot;
+        const int e = block_excl_sum(x, wtot, tot);
+        if (cc < nch) off2[cc] = run2 + e;
+        run2 += tot;
+      }
+      __syncthreads();
+      // stage in token order: ballot ranks inside each chunk slice
+      const unsigned long long below = (1ull << lane) - 1ull;
+      int pos = 0;
+      sweep([&](uint2 e, bool ok) {
+        const bool keep = ok && e.x >= cut;
+        const unsigned long long bk = __ballot(keep);
+        if (keep) surv[pos + __popcll(bk & below)] = e;
+        pos += __popcll(bk);
+      }, [&](int c) { pos = off2[c]; }, none);
+      for (int b = tid; b < 3 * kTkBins; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
+      __syncthreads();
+      n = run2;
+      base = cut;
+      staged = true;
+      narrowed = true;
+    } else {  // (only with more than kTkStage keys equal to the K-th)
+      for (int b = tid; b < 3 * kTkBins; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
+      __syncthreads();
+    }
+  }
   const uint32_t range = raw ? 0xFFFFFFFFu : kmax - base;
   const int B = range == 0u ? 0 : 32 - __clz(range);  // bits of (key - base)
   const int s1 = B > 12 ? B - 12 : 0;
@@ -272,7 +369,7 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   };
 
   // 2. first digit (bits s1 .. B-1 of key - base), staging into LDS on the way
-  if (staged) {
+  if (staged && !narrowed) {
     constexpr int U = 4;
     for (int x0 = tid; x0 < n; x0 += U * kTkSelThreads) {
       uint2 e[U];
@@ -370,6 +467,8 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
     uint32_t nb;
     if (n >= K + K / 4) {
       nb = base + ((uint32_t)bn << s1);
+    } else if (narrowed) {
+      nb = nb0;
     } else {
       const uint32_t d = (T - base) + (1u << s1);
       nb = base > d ? base - d : 0u;

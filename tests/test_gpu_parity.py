@@ -236,9 +236,12 @@ def test_device_error_on_index_past_context():
 
 
 def test_topk_both_paths_in_one_batch():
-    """Contexts on both sides of the one-workgroup limit (256K tokens) in one
-    call: the single-workgroup and the multi-workgroup kernels each take
-    their requests, with ties, -0.0 and an empty request."""
+    """Long contexts (up to 300K tokens) in one call, with ties, -0.0 and an
+    empty request. On the first call (no bound yet) every score survives the
+    filter: the select narrows them to a cut by histogram passes, except for
+    the all-equal request, whose ties at the K-th value exceed what LDS can
+    stage and which takes the unstaged path; the second call starts from the
+    bound the first one left."""
     rng = np.random.default_rng(5)
     max_ctx, K = 300000, 2048
     lens = [300000, 262145, 262144, 70001, 0, 290000]
