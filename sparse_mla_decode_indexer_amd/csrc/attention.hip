@@ -12,8 +12,9 @@
 // takes 64 query rows (4 blocks of 16) of one request and a contiguous
 // split of its plan, 32 rows (a tile) at a time:
 //   - rows are fetched straight from the pool into LDS (global_load_lds,
-//     no registers), double-buffered: tile t+1 is in flight while tile t is
-//     computed; fp8 codes land raw and are widened to bf16 in LDS (exact);
+//     no registers), through a ring of three buffers: tiles t+1 and t+2
+//     are in flight while tile t is computed, and the queries load under
+//     the first gathers; fp8 codes land raw and are widened to bf16 in LDS (exact);
 //     absent rows read a zero row; rows sit 73 chunks of 16 bytes apart in
 //     LDS (one pad chunk), so the MFMA operand reads of 16 rows at one
 //     column hit distinct banks and operand addresses are a base plus an
@@ -33,7 +34,8 @@
 //     P^T;
 //   - two workgroup barriers per tile: tile landed / previous tile retired,
 //     and the partial-score exchange.
-// Softmax is online (running max and sum in fp32, base 2). With more than
+// Softmax is online (fp32, base 2): a reference maximum that moves only
+// when a score passes it by more than 2^8, and a running sum. With more than
 // one split, each split writes a normalised partial output and its
 // log-sum-exp; k_attn_combine merges them.
 //
@@ -64,8 +66,21 @@ constexpr int kRawChunks = kRowDim / 16;         // 36 chunks per fp8 row
 constexpr int kRawTileBytes = kTile * kRawChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.f;  // see the online softmax in k_attn_mfma
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// LDS transpose load of 4 x 16 bits (ds_read_b64_tr_b16): within each group
+// of 16 lanes, output lane j receives element j % 4 of the 8 bytes addressed
+// by lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4, in that order.
+__device__ inline u32x2_t tr_load(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
 
 __device__ inline f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -127,11 +142,16 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
     float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o,
     float* __restrict__ part_lse, uint32_t* __restrict__ err) {
-  // Two distinct LDS buffers (not one indexed array) so that the compiler
-  // can tell the DMA into one from the reads of the other and does not wait
-  // for the prefetch before computing.
-  __shared__ __attribute__((aligned(16))) uint8_t bufA[FP8 ? kRawTileBytes : kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t bufB[FP8 ? kRawTileBytes : kTileBytes];
+  // A ring of three distinct LDS buffers (not one indexed array) so that
+  // the compiler can tell the DMA into one from the reads of another and
+  // does not wait for the prefetch before computing. Each holds a tile plus
+  // the landing area of the padding DMAs (see issue below).
+  constexpr int kPos = FP8 ? kTile * kRawChunks : kTilePos;  // chunk positions of a tile
+  constexpr int kIssue = (kPos + 128 * QB - 1) / (128 * QB);  // DMAs per thread and tile
+  constexpr int kBufBytes = kIssue * 128 * QB * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t bufA[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t bufB[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t bufC[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wide[FP8 ? kTileBytes : 16];
   __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
   __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
@@ -150,7 +170,8 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   const int t_begin = sp * tiles_per_split;
   const int nt = min(n_tiles, t_begin + tiles_per_split) - t_begin;
 
-  // plan rows (and fp8 scales) of this split
+  // plan rows (and fp8 scales) of this split; the query loads below stay in
+  // flight across the barrier and the first gathers
   for (int j = tid; j < nt * kTile; j += kAttThreads) {
     const int jj = t_begin * kTile + j;
     int pr = jj < K ? pl[jj] : -1;
@@ -162,62 +183,74 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     if (FP8) scale_s[j] = pr >= 0 ? pool_scales[pr] : 0.f;
   }
   // Q^T operand for key dims 288*half .. +288: lane holds query row qh,
-  // dims 288*half + 32*kk + 8*kg .. +8
+  // dims 288*half + 32*kk + 8*kg .. +8. Lanes past the last query row
+  // compute on row 0 and write nothing. The registers are first read by the
+  // first tile's QK, so the loads overlap the first gathers.
   constexpr int kKSteps = kRowDim / 64;  // 9
   u32x4_t qop[kKSteps];
   {
     const uint16_t* qr = q + ((size_t)i * QR + (qvalid ? qh : 0)) * kRowDim + 288 * half;
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * kg);
-      qop[kk] = qvalid ? x : u32x4_t{0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < kKSteps; ++kk) qop[kk] = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * kg);
   }
-  __syncthreads();
+  lds_sync();
 
-  // Start the gather of tile t into `dst` (wave-contiguous LDS targets).
-  auto issue = [&](int t, uint8_t* dst) {
-    if (!FP8) {
+  // Gather of a tile into LDS (wave-contiguous LDS targets). This thread's
+  // chunk positions p = k * threads + tid are the same in every tile; their
+  // plan rows are read from LDS one tile ahead of the DMA, off the critical
+  // path. Every wave issues exactly kIssue DMAs per tile, with every lane
+  // active: positions past the tile, pad chunks, absent rows and tiles past
+  // the split read the zero row. With a fixed count per tile the wait for a
+  // tile is a constant vmcnt, and the compiler, which counts the same
+  // instructions, sees that the tile is complete and adds no wait of its own.
+  constexpr int kRowChunksT = FP8 ? kRawChunks : kRowChunks;
+  auto rows_of = [&](int t, int* rr) {
 #pragma unroll
-      for (int k = 0; k < (kTilePos + kAttThreads - 1) / kAttThreads; ++k) {
-        const int p = k * kAttThreads + tid;
-        if (k * kAttThreads + wave * 64 < kTilePos) {  // wave-uniform
-          const int r = p / kRowChunks, c = p - r * kRowChunks;
-          if (p < kTilePos && c < kChunks) {  // pad chunks are never read
-            const int pr = prow_s[t * kTile + r];
-            const uint8_t* src = pr >= 0 ? pool + (size_t)pr * (2 * kRowDim) + c * 16 : zero_row + c * 16;
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16),
-                                             16, 0, 0);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < (kTile * kRawChunks + kAttThreads - 1) / kAttThreads; ++k) {
-        const int p = k * kAttThreads + tid;
-        if (k * kAttThreads + wave * 64 < kTile * kRawChunks) {
-          const int r = p / kRawChunks, c = p - r * kRawChunks;
-          const int pr = prow_s[t * kTile + r];
-          const uint8_t* src = pr >= 0 ? pool + (size_t)pr * kRowDim + c * 16 : zero_row + c * 16;
-          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16),
-                                           16, 0, 0);
-        }
-      }
+    for (int k = 0; k < kIssue; ++k) {
+      const int p = k * kAttThreads + tid;
+      const int r = min(p / kRowChunksT, kTile - 1);
+      rr[k] = t < nt ? prow_s[t * kTile + r] : -1;
     }
   };
+  auto issue = [&](const int* rr, uint8_t* dst) {
+#pragma unroll
+    for (int k = 0; k < kIssue; ++k) {
+      const int p = k * kAttThreads + tid;
+      const int r = p / kRowChunksT, c = p - r * kRowChunksT;  // c <= 72
+      const bool real = rr[k] >= 0 && p < kPos && (FP8 || c < kChunks);
+      const size_t rb = FP8 ? kRowDim : 2 * kRowDim;
+      const uint8_t* src = real ? pool + (size_t)rr[k] * rb + c * 16 : zero_row + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16), 16, 0, 0);
+    }
+  };
+  // vmcnt(n) with expcnt and lgkmcnt left alone (n < 16)
+  constexpr int kWaitOne = 0xF70 | kIssue;      // all but the last tile issued
+  constexpr int kWaitTwo = 0xF70 | 2 * kIssue;  // all but the last two tiles issued
+  static_assert(2 * kIssue < 16, "vmcnt immediate");
 
-  f32x4_t acc[2][8];
+  // O^T accumulators: block b holds dims 256*half + 16b + 4kg + v (v = 0..3)
+  // of query ln
+  f32x4_t acc[16];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 16; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // V^T operand reads (LDS transpose loads): in each 16-lane group, source
+  // lane 4i + c reads dims 4c .. 4c+3 of row krow(kg, i) (first load) or
+  // krow(kg, 4 + i) (second), and lane ln of the group receives dim ln of
+  // those four rows: the A operand of 16 dims over rows krow(kg, 0..7).
+  const int tr_i = (lane & 15) >> 2, tr_c = lane & 3;
+  const int v_off0 = krow(kg, tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
+  const int v_off1 = krow(kg, 4 + tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
   float m_run = -INFINITY, lpart = 0.f;
 
-  // One tile: wait for it, start the next gather into `nxt`, compute on `cur`.
+  // One tile: wait for it, start the gather of tile t + 2 into `nxt` (the
+  // buffer of tile t - 1), compute on `cur`. Tiles t and t + 1 are in flight
+  // on entry (the latter possibly a padding gather).
+  int rows_next[kIssue];
   auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile t has landed
-    lds_sync();                      // all of tile t is in LDS; tile t-1 is done
-    if (t + 1 < nt) issue(t + 1, nxt);
+    __builtin_amdgcn_s_waitcnt(kWaitOne);  // this wave's part of tile t has landed
+    lds_sync();                            // all of tile t is in LDS; tile t-1 is done
+    issue(rows_next, nxt);
+    rows_of(t + 3, rows_next);
     const uint8_t* T = FP8 ? wide : cur;
     if (FP8) {  // widen the raw codes of tile t into the bf16 tile
       for (int x = tid; x < kTile * kRawChunks; x += kAttThreads) {
@@ -260,9 +293,14 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       pm = fmaxf(pm, s[e]);
     }
     pm = max_across_kg(pm);
-    const float m_new = fmaxf(m_run, pm);
+    // The reference maximum moves only when a score passes it by more than
+    // kLazyMax (base-2 units), so the accumulators are rarely rescaled; the
+    // weights then stay below 2^kLazyMax, far inside fp32 and bf16 range.
+    const bool grow = pm > m_run + kLazyMax;  // also the first finite maximum
+    const bool rescale = grow && m_run != -INFINITY;
+    const float m_new = grow ? pm : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : (grow ? 0.f : 1.f);
     m_run = m_new;
     u32x4_t bhi, blo;  // P^T operand (hi and lo parts), rows krow(kg, 0..7)
     {
@@ -282,41 +320,46 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       }
     }
 
-    // PV: dims 256*half .. +256 of this wave's 16 queries
-    if (__any(alpha != 1.f)) {  // the running max moved for some query of this wave
+    // PV: dims 256*half .. +256 of this wave's 16 queries, 16 at a time
+    if (__any(rescale)) {  // the reference max moved for some query of this wave
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
+      for (int b = 0; b < 16; ++b) acc[b] *= alpha;
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      u32x4_t R[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        R[j] = *reinterpret_cast<const u32x4_t*>(T + swz(krow(kg, j), 32 * half + 16 * g + ln) * 16);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4_t A0, A1;  // dims 8*ln + 2w and 8*ln + 2w + 1 over rows krow(kg, 0..7)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t x = R[2 * d][w], y = R[2 * d + 1][w];
-          A0[d] = (x & 0xFFFFu) | (y << 16);
-          A1[d] = (x >> 16) | (y & 0xFFFF0000u);
-        }
-        acc[g][2 * w] = mfma16(A0, bhi, acc[g][2 * w]);
-        acc[g][2 * w + 1] = mfma16(A1, bhi, acc[g][2 * w + 1]);
-        acc[g][2 * w] = mfma16(A0, blo, acc[g][2 * w]);
-        acc[g][2 * w + 1] = mfma16(A1, blo, acc[g][2 * w + 1]);
-      }
+    for (int b = 0; b < 16; ++b) {
+      const u32x2_t x = tr_load(T + v_off0 + 32 * b);
+      const u32x2_t y = tr_load(T + v_off1 + 32 * b);
+      const u32x4_t A = u32x4_t{x[0], x[1], y[0], y[1]};
+      acc[b] = mfma16(A, bhi, acc[b]);
+      acc[b] = mfma16(A, blo, acc[b]);
     }
   };
 
-  issue(0, bufA);
-  for (int t = 0; t < nt; t += 2) {
-    tile(t, bufA, bufB);
+  {
+    int rr[kIssue];
+    rows_of(0, rr);
+    issue(rr, bufA);
+    rows_of(1, rr);
+    issue(rr, bufB);
+    rows_of(2, rows_next);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitTwo);  // the query loads (issued before the gathers)
+  // Full turns of the ring, then the 0-2 remaining tiles: every path issues
+  // the same number of gathers per tile, so the compiler's count of pending
+  // loads matches the waits above at every tile.
+  int t = 0;
+  for (; t + 3 <= nt; t += 3) {
+    tile(t, bufA, bufC);
+    tile(t + 1, bufB, bufA);
+    tile(t + 2, bufC, bufB);
+  }
+  if (t < nt) {
+    tile(t, bufA, bufC);
     if (t + 1 < nt) tile(t + 1, bufB, bufA);
   }
+  // the two padding gathers issued by the last tiles land before the wave
+  // ends (they were issued a tile earlier, so this rarely waits)
+  __builtin_amdgcn_s_waitcnt(0xF70);
 
   // softmax denominator: sum over the 4 lanes (row groups) of each query
   const float l = sum_across_kg(lpart);
@@ -332,17 +375,11 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     dst = part_o + prow * kNope;
     if (kg == 0 && half == 0) part_lse[prow] = lse2;
   }
-  // lane holds dims 256*half + 128g + 32kg + 8v + c, c = 0..7, v = 0..3
+  // lane holds dims 256*half + 16b + 4kg + v, v = 0..3
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float* o = dst + 256 * half + 128 * g + 32 * kg + 8 * v;
-      *reinterpret_cast<float4*>(o) = make_float4(acc[g][0][v] * inv, acc[g][1][v] * inv,
-                                                  acc[g][2][v] * inv, acc[g][3][v] * inv);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[g][4][v] * inv, acc[g][5][v] * inv,
-                                                      acc[g][6][v] * inv, acc[g][7][v] * inv);
-    }
+  for (int b = 0; b < 16; ++b)
+    *reinterpret_cast<float4*>(dst + 256 * half + 16 * b + 4 * kg) =
+        make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv);
 }
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
@@ -358,28 +395,35 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
   if (row >= n_rows) return;
   const int i = row / QR, qh = row - i * QR;
   const size_t base = (size_t)i * n_splits * QR + qh;  // partial row of split s: base + s * QR
+  // One pass: the log-sum-exps and partial outputs of a batch of splits are
+  // loaded together, the sums are rescaled when the running maximum moves.
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_lse[base + (size_t)s * QR]);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.f;
-  if (M != -INFINITY) {
-    constexpr int kBatch = 16;  // partial loads in flight per thread
-    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
-      float w[kBatch];
-      float4 x[kBatch];
+  constexpr int kBatch = 16;  // partial loads in flight per thread
+  for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+    float w[kBatch];
+    float4 x[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int s = min(s0 + u, n_splits - 1);
-        const size_t pr = base + (size_t)s * QR;
-        w[u] = s0 + u < n_splits ? part_lse[pr] : -INFINITY;
-        x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
-      }
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = min(s0 + u, n_splits - 1);
+      const size_t pr = base + (size_t)s * QR;
+      w[u] = s0 + u < n_splits ? part_lse[pr] : -INFINITY;
+      x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
+    }
+    float mb = M;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float e = __builtin_amdgcn_exp2f(w[u] - M);  // 0 for the padding entries
-        W += e;
-        o.x += e * x[u].x; o.y += e * x[u].y; o.z += e * x[u].z; o.w += e * x[u].w;
-      }
+    for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, w[u]);
+    if (mb == -INFINITY) continue;  // nothing attended so far
+    const float f = __builtin_amdgcn_exp2f(M - mb);  // 0 while M is -inf
+    W *= f;
+    o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+    M = mb;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float e = __builtin_amdgcn_exp2f(w[u] - M);  // 0 for empty splits and padding
+      W += e;
+      o.x += e * x[u].x; o.y += e * x[u].y; o.z += e * x[u].z; o.w += e * x[u].w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;

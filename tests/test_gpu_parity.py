@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gpu_helpers import Runner, log, small
-from oracle import select_topk
+from oracle import mla_attention, select_topk
 from sparse_mla_decode_indexer_amd import workload as W
 from sparse_mla_decode_indexer_amd.pool import TieredPool
 
@@ -266,6 +266,70 @@ def test_topk_both_paths_in_one_batch():
             got = idx.cpu().numpy()
             for r, L in enumerate(lens):
                 assert np.array_equal(got[r], select_topk(sc[r], L, K)), f"req {r} L={L} rep {rep}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("shape", ["rising", "jumps", "falling", "one_dominant"])
+def test_attention_score_jumps(kv, shape):
+    """The kernel's softmax keeps a reference maximum that moves only when a
+    score passes it by more than 2^8. Scores that climb slowly (rising: the
+    reference moves now and then, weights up to ~2^8 in between, about 8
+    rows share the weight), climb by far more than that from tile to tile
+    (jumps), start high and decay (falling), or are set by one row in the
+    last tile (one_dominant), with absent plan entries mixed in: every head
+    within the fp64 bar."""
+    from oracle import bf16_decode, e4m3fn_decode
+    from gpu_helpers import ATTN_TOL, LSE_TOL, attn_rel_err
+    rng = np.random.default_rng({"rising": 1, "jumps": 4, "falling": 2, "one_dominant": 3}[shape])
+    K, H, n_rows = 2048, 128, 4096
+    pool = TieredPool(page_size=64, num_pool_pages=n_rows // 64, max_requests=1, max_context=n_rows,
+                      kv_dtype=kv, top_k=K, hot_rows=4096, max_batch=1, max_q_rows=H, host_rows=64)
+    try:
+        x = rng.standard_normal((n_rows, W.ROW_DIM)).astype(np.float32)
+        plan = rng.permutation(n_rows)[:K].astype(np.int32)
+        plan[rng.integers(0, K, 40)] = -1
+        plan[-7:] = -1
+        tile = np.arange(K) // 32
+        if shape == "rising":
+            f = 1.0 + 0.05 * tile
+        elif shape == "jumps":
+            f = 1.0 + 2.0 * tile
+        elif shape == "falling":
+            f = 1.0 + 2.0 * (tile.max() - tile)
+        else:
+            f = np.full(K, 0.5)
+        q = rng.standard_normal((H, W.ROW_DIM)).astype(np.float32)
+        live = plan >= 0
+        x[plan[live]] *= f[live, None].astype(np.float32)
+        if shape == "one_dominant":
+            j = int(np.flatnonzero(live)[-1])
+            x[plan[j]] = 3.0 * q[5]          # head 5 puts nearly all weight on it
+        sm = 1.0 / np.sqrt(W.ROW_DIM)
+        if kv == "bf16":
+            bits = W.f32_to_bf16_bits(x)
+            pool.pool_row_view().copy_(torch.from_numpy(bits.view(np.uint8).reshape(n_rows, -1)).cuda())
+            logical = bf16_decode(bits)
+        else:
+            codes, sc = W.f32_rows_to_fp8(x)
+            pool.pool_row_view().copy_(torch.from_numpy(codes).cuda())
+            pool.pool_scales.copy_(torch.from_numpy(sc).cuda())
+            logical = e4m3fn_decode(codes) * sc[:, None].astype(np.float64)
+        qb = W.f32_to_bf16_bits(q)
+        d_q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16).reshape(1, 1, H, W.ROW_DIM)
+        d_plan = torch.from_numpy(plan).cuda().reshape(1, K)
+        out = torch.full((1, 1, H, W.NOPE_DIM), np.nan, device="cuda")
+        lse = torch.full((1, 1, H), np.nan, device="cuda")
+        pool.sparse_mla_decode(d_q, d_plan, sm, out, lse)
+        o = out.cpu().numpy().reshape(H, -1)
+        l = lse.cpu().numpy().reshape(H)
+        o_ref, l_ref = mla_attention(bf16_decode(qb), logical[plan[live]], sm)
+        e = attn_rel_err(o, o_ref)
+        assert e <= ATTN_TOL, f"{kv} {shape}: attention rel err {e:.3e}"
+        le = float(np.max(np.abs(l - l_ref) / np.maximum(1.0, np.abs(l_ref))))
+        assert le <= LSE_TOL, f"{kv} {shape}: lse err {le:.3e}"
         assert pool.device_error()[0] == 0
     finally:
         pool.close()
