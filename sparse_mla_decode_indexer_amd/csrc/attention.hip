@@ -521,7 +521,7 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   // on the tiles per split so that the fixed cost per workgroup (plan,
   // queries, partial output) is amortised.
   static const int forced = env_int("HS_ATTN_TILES_PER_SPLIT", 0);
-  constexpr int min_tps = 4;
+  constexpr int min_tps = 2;
   int tps;
   if (forced > 0) {
     tps = forced;

@@ -11,7 +11,7 @@
 //     and rewrites the LRU order with ordered compactions in LDS, updates
 //     tags / stamps / reverse map, writes the plan and the counts, and
 //     publishes the plan with a per-request flag;
-//   copy workgroup (request i, part c), one per 16 plan positions (4 per
+//   copy workgroup (request i, part c), one per 64 plan positions (4 per
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
 //     store over PCIe right away, then waits for the flag and writes the
@@ -19,9 +19,13 @@
 //     slots (rows it did not guess are read then). The guess only decides
 //     how early the PCIe reads start; which rows are written comes from the
 //     bookkeeper.
-// Bookkeeper thread t owns plan positions [tP, tP + P) and LRU positions
-// [tQ, tQ + Q) (P, Q powers of two, Q >= 4), so each ordered compaction is
-// one block-wide scan.
+// Bookkeeper thread t owns plan positions t + 1024 e (e < P), so wave w
+// holds plan positions 1024 e + 64 w .. + 63: one miss-mask word per wave
+// and e, from a ballot, and token-order ranks from per-wave counts. It owns
+// LRU positions [tQ, tQ + Q) (P, Q powers of two, Q >= 4), so each ordered
+// compaction of the LRU order is one block-wide scan. The request's page
+// table is staged in LDS when it fits (kRsPtLds entries), so that only the
+// reverse-map lookups are scattered global loads.
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
 // bounded (a device error is raised past the bound and the copy skipped).
@@ -63,7 +67,8 @@ struct RsArgs {
   const int32_t* idx;
   const int32_t* req_ids;
   int n_req;
-  int P, Q;  // plan and LRU positions per bookkeeper thread
+  int P, Q;    // plan and LRU positions per bookkeeper thread
+  int pt_lds;  // page-table entries staged in LDS (0: look up in global memory)
   int32_t* plan_out;
   int32_t* counts_out;
   const uint8_t* host_rows;
@@ -72,19 +77,22 @@ struct RsArgs {
   float* pool_scales;
 };
 
+constexpr int kRsPtLds = 8192;  // page-table entries a bookkeeper stages in LDS, at most
+
 struct RsStatic {
   int tmp[kRsWaves + 1];
-  uint32_t mword[kMaxTopK / 32];  // miss bits, 32 plan positions per word
+  int wmiss[kRsPos * kRsWaves];      // misses per (e, wave), then their exclusive prefix
   int n_res, n_hot;
   int role;
   int go;
 };
 
-// Dynamic LDS of a bookkeeper, with Spad = 256 Q >= S: lru[Spad] and
+// Dynamic LDS of a bookkeeper, with Spad = 1024 Q >= S: lru[Spad] and
 // tag[Spad] int32 (padded with -1), victims[K] int32, hot_pages[HP] int32,
-// flag[Spad] uint8 (bit0: hit this step, bit1: victim).
-__host__ __device__ inline size_t rs_dyn_bytes(int Spad, int K, int HP) {
-  return 8 * (size_t)Spad + 4 * (size_t)K + 4 * (size_t)HP + (size_t)Spad;
+// page table[PT] int32, flag[Spad] uint8 (bit0: hit this step, bit1:
+// victim).
+__host__ __device__ inline size_t rs_dyn_bytes(int Spad, int K, int HP, int PT) {
+  return 8 * (size_t)Spad + 4 * (size_t)K + 4 * (size_t)HP + 4 * (size_t)PT + (size_t)Spad;
 }
 
 // The bookkeeper issues every global load before its first global store
@@ -138,7 +146,10 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   int32_t* tag_l = lru + Spad;
   int32_t* vic = tag_l + Spad;
   int32_t* hp = vic + K;
-  uint8_t* flag = reinterpret_cast<uint8_t*>(hp + HP);
+  int32_t* ptl = hp + HP;
+  uint8_t* flag = reinterpret_cast<uint8_t*>(ptl + a.pt_lds);
+  const int npg = (L + ps - 1) >> lps;  // pages of the context
+  const bool pt_in_lds = npg > 0 && npg <= a.pt_lds;
 
   // 0. loads: LRU order and slot tags (coalesced, then to LDS), hot pages;
   //    this thread's selected tokens, then their page-table and reverse-map
@@ -164,17 +175,21 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     }
   }
   for (int p = tid; p < HP; p += kRsThreads) hp[p] = hp_g[p];
-  for (int w = tid; w < 2 * sc.words; w += kRsThreads) st.mword[w] = 0u;
+  if (pt_in_lds)
+    for (int p = tid; p < npg; p += kRsThreads) ptl[p] = pt[p];
   if (tid == 0) st.n_res = st.n_hot = 0;
+  const int lane = tid & 63, wave = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1ull;
   int tok[kRsPos], code[kRsPos];  // code: pool row, -1 nothing, -2 miss
   uint32_t missbits = 0u;  // bit e: position e of this thread is a miss
-  int M, mbase;
+  unsigned long long mb[kRsPos];  // miss bits of this wave's 64 positions of each e
+  int M;
   {
     int g[kRsPos], sl[kRsPos];
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
-        const int j = tid * P + e;
+        const int j = e * kRsThreads + tid;
         const int t = sel[min(j, K - 1)];
         tok[e] = j < K ? t : -1;
       }
@@ -184,7 +199,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       if (e < P) {
         const int t = tok[e];
         const int tt = (t >= 0 && t < L) ? t : 0;  // an in-range address either way
-        g[e] = pt[tt >> lps];
+        if (!pt_in_lds) g[e] = pt[tt >> lps];
         sl[e] = rev[tt];
       }
     }
@@ -194,15 +209,17 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
+        const int t = tok[e];
+        const int tt = (t >= 0 && t < L) ? t : 0;
+        if (pt_in_lds) g[e] = ptl[tt >> lps];
         hpg[e] = hp[min(max(sl[e], 0), S - 1) >> lps];
       }
     }
-    int nm = 0, nr = 0, nh = 0;
     int bad_tok = -1, bad_slot = -1;  // first offending entry of this thread
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
-        const int j = tid * P + e;
+        const int j = e * kRsThreads + tid;
         const int t = tok[e];
         const bool ok = t >= 0 && t < L;
         const bool res = ok && g[e] >= 0;
@@ -212,19 +229,35 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
         bad_tok = (bad_tok < 0 && j < K && t >= L) ? t : bad_tok;
         bad_slot = (bad_slot < 0 && cand && !hot) ? sl[e] : bad_slot;
         if (hot) flag[sl[e]] = 1;
-        if (miss) atomicOr(&st.mword[j >> 5], 1u << (j & 31));
         missbits |= miss ? (1u << e) : 0u;
         code[e] = res ? g[e] * ps + (t & (ps - 1)) : hot ? hpg[e] * ps + (sl[e] & (ps - 1)) : miss ? -2 : -1;
-        nr += res ? 1 : 0;
-        nh += hot ? 1 : 0;
-        nm += miss ? 1 : 0;
+        mb[e] = __ballot(miss);
+        const int nr = __popcll(__ballot(res)), nh = __popcll(__ballot(hot));
+        if (lane == 0) {
+          st.wmiss[e * kRsWaves + wave] = __popcll(mb[e]);
+          if (nr) atomicAdd(&st.n_res, nr);
+          if (nh) atomicAdd(&st.n_hot, nh);
+        }
       }
     }
     if (bad_tok >= 0) raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)bad_tok);
     if (bad_slot >= 0) raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)bad_slot);
-    if (nr) atomicAdd(&st.n_res, nr);
-    if (nh) atomicAdd(&st.n_hot, nh);
-    mbase = block_excl_sum(nm, st.tmp, M);  // misses rank in token order
+    __syncthreads();
+    // token-order rank base of each (e, wave): exclusive prefix over e-major
+    // (e, wave) of the per-wave miss counts (wave 0; P * 16 <= 64 entries)
+    if (wave == 0) {
+      const int c = lane < P * kRsWaves ? st.wmiss[lane] : 0;
+      int x = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane < P * kRsWaves) st.wmiss[lane] = x - c;
+      if (lane == 63) st.tmp[0] = x;
+    }
+    __syncthreads();
+    M = st.tmp[0];
   }
   // 2. untouched slots in LRU order (thread t holds LRU positions [tQ, tQ+Q));
   //    the first M of them are the victims
@@ -294,12 +327,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   int vs[kRsPos];
   {
     int hv[kRsPos];
-    int mr = mbase;
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
+        const int mr = st.wmiss[e * kRsWaves + wave] + __popcll(mb[e] & below);  // misses before j
         vs[e] = vic[min(mr, max(M - 1, 0))];
-        mr += code[e] == -2 ? 1 : 0;
       }
     }
 #pragma unroll
@@ -319,11 +351,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   // 4. plan and miss words, then the flag
 #pragma unroll
   for (int e = 0; e < kRsPos; ++e) {
-    const int j = tid * P + e;
+    const int j = e * kRsThreads + tid;
     if (e < P && j < K) put(&plan[j], code[e] >= 0 ? code[e] : -1);
+    const int w = e * kRsWaves + wave;  // word of positions 64 w .. 64 w + 63
+    if (e < P && lane == 0 && w < sc.words) put_word(w, mb[e]);
   }
-  for (int w = tid; w < sc.words; w += kRsThreads)
-    put_word(w, (unsigned long long)st.mword[2 * w] | ((unsigned long long)st.mword[2 * w + 1] << 32));
   publish();
   // 5. LRU state: the untouched non-victims keep their order at the front,
   //    then the hit and victim slots in ascending slot number, all with
@@ -519,9 +551,11 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   RsArgs a{idx, req_ids, n_req,
            pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
            max(4, pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads)),
+           v.pages_per_req <= kRsPtLds ? v.pages_per_req : 0,
            plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
            p->host_scales, p->pool_rows, p->pool_scales};
-  const size_t dyn = (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req) + 15) & ~(size_t)15;
+  const size_t dyn =
+      (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req, a.pt_lds) + 15) & ~(size_t)15;
   const int grid = n_req * (1 + sc.parts);
   switch (p->d.kv_dtype) {
     case HS_F32:
