@@ -89,7 +89,9 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   of.tk_max = take(4 * B * max_chunks);
   of.tk_cand = take(8 * B * max_chunks * kTkChunk);
   of.tk_bound = take(4 * R);
-  of.rs_miss_mask = take(8 * B * ((K + 63) / 64));
+  of.rs_mdst = take(4 * B * (size_t)K);
+  of.rs_mslot = take(4 * B * (size_t)K);
+  of.rs_mold = take(4 * B * (size_t)K);
   of.rs_flag = take(4 * B);
   of.rs_exit = take(4 * B);
   of.rs_ticket = take(8);

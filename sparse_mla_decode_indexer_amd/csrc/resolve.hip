@@ -8,20 +8,22 @@
 // counter in the order workgroups start:
 //   bookkeeper (tickets 0 .. n_req-1), one per request: classifies the K
 //     tokens (resident > hot > miss), stamps the hit slots, picks the victims
-//     and rewrites the LRU order with ordered compactions in LDS, updates
-//     tags / stamps / reverse map, writes the plan and the counts, and
-//     publishes the plan with a per-request flag;
+//     and rewrites the LRU order with ordered compactions in LDS, writes the
+//     plan, the copy destination, hot slot and that slot's old token of
+//     every missed position and the counts, and publishes the plan with a
+//     per-request flag;
 //   copy workgroup (request i, part c), one per 64 plan positions (4 per
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
-//     store over PCIe right away, then waits for the flag and writes the
-//     rows the bookkeeper actually classified as misses into their hot
-//     slots (rows it did not guess are read then). The guess only decides
+//     store over PCIe right away; each wave then waits for the flag and
+//     writes the rows the bookkeeper actually classified as misses into
+//     their hot slots (rows it did not guess are read then), and moves the
+//     slots' tags and reverse-map entries from the old tokens to the new. The guess only decides
 //     how early the PCIe reads start; which rows are written comes from the
 //     bookkeeper.
 // Bookkeeper thread t owns plan positions t + 1024 e (e < P), so wave w
-// holds plan positions 1024 e + 64 w .. + 63: one miss-mask word per wave
-// and e, from a ballot, and token-order ranks from per-wave counts. It owns
+// holds plan positions 1024 e + 64 w .. + 63 and the token-order rank of a
+// miss comes from a ballot and per-wave counts. It owns
 // LRU positions [tQ, tQ + Q) (P, Q powers of two, Q >= 4), so each ordered
 // compaction of the LRU order is one block-wide scan. The request's page
 // table is staged in LDS when it fits (kRsPtLds entries), so that only the
@@ -48,11 +50,12 @@ namespace hs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RsScratch {
-  unsigned long long* miss_mask;  // [batch][words] miss bits of 64 plan positions
+  int32_t* mdst;                  // [batch][K] pool row a missed position is copied to, else -1
+  int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
+  int32_t* mold;                  // [batch][K] token that slot held before (or -1)
   uint32_t* flag;                 // [batch] 1 once request i's plan is published
   uint32_t* exit_cnt;             // [batch] copy workgroups of request i done
   uint32_t* ticket;               // [2] roles handed out, workgroups exited
-  int words;                      // ceil(K / 64) mask words per request
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
 
@@ -84,7 +87,6 @@ struct RsStatic {
   int wmiss[kRsPos * kRsWaves];      // misses per (e, wave), then their exclusive prefix
   int n_res, n_hot;
   int role;
-  int go;
 };
 
 // Dynamic LDS of a bookkeeper, with Spad = 1024 Q >= S: lru[Spad] and
@@ -108,14 +110,14 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   const int32_t* sel = a.idx + (size_t)i * K;
   int32_t* plan = a.plan_out + (size_t)i * K;
   const int r0 = a.req_ids[i];
-  // What the copy workgroups read (plan, miss words, flag) is written with
+  // What the copy workgroups read (plan, copy destinations, flag) is written with
   // device-coherent stores; the flag goes out once this workgroup's stores
   // of the rest have completed. The LRU state is written afterwards: no copy
   // workgroup reads it, and the flag does not wait for it.
   auto put = [](int32_t* p, int x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  auto put_word = [&](int w, unsigned long long x) {
-    __hip_atomic_store(&sc.miss_mask[(size_t)i * sc.words + w], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
+  int32_t* mdst = sc.mdst + (size_t)i * K;
+  int32_t* mslot = sc.mslot + (size_t)i * K;
+  int32_t* mold = sc.mold + (size_t)i * K;
   auto publish = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
@@ -128,14 +130,20 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, (uint32_t)r0);
       if (a.counts_out) a.counts_out[3 * i] = a.counts_out[3 * i + 1] = a.counts_out[3 * i + 2] = 0;
     }
-    for (int j = tid; j < K; j += kRsThreads) put(&plan[j], -1);
-    for (int w = tid; w < sc.words; w += kRsThreads) put_word(w, 0ull);
+    for (int j = tid; j < K; j += kRsThreads) {
+      put(&plan[j], -1);
+      put(&mdst[j], -1);
+      put(&mslot[j], -1);
+    }
     publish();
     return;
   }
   const int r = r0;
   const int L = v.ctx_len[r];
   const int n = v.step[r] + 1;
+  int cnt0[3];  // running counters, loaded before the first store
+#pragma unroll
+  for (int k = 0; k < 3; ++k) cnt0[k] = tid == 0 ? v.counters[3 * r + k] : 0;
   const int32_t* pt = v.page_table + (size_t)r * v.pages_per_req;
   int32_t* rev = v.rev + (size_t)r * v.max_context;
   int32_t* tag = v.slot_tag + (size_t)r * S;
@@ -174,6 +182,14 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       }
     }
   }
+  // this thread's slot stamps, updated in place at the end (whole 16 bytes)
+  const bool stamp4 = (S & 3) == 0;
+  int4 st4[kRsSlots / 4];
+#pragma unroll
+  for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+    const int x = tid * Q + 4 * e4;
+    if (4 * e4 < Q && stamp4 && x < S) st4[e4] = reinterpret_cast<const int4*>(stamp)[x >> 2];
+  }
   for (int p = tid; p < HP; p += kRsThreads) hp[p] = hp_g[p];
   if (pt_in_lds)
     for (int p = tid; p < npg; p += kRsThreads) ptl[p] = pt[p];
@@ -204,6 +220,8 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       }
     }
     __syncthreads();  // LDS tables ready
+    // keep the counter loads here, ahead of every store (not sunk to their use)
+    asm volatile("" : "+v"(cnt0[0]), "+v"(cnt0[1]), "+v"(cnt0[2]));
     // 1. classify: resident > hot > miss (hit flags in LDS, no stores yet)
     int hpg[kRsPos];
 #pragma unroll
@@ -261,7 +279,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   }
   // 2. untouched slots in LRU order (thread t holds LRU positions [tQ, tQ+Q));
   //    the first M of them are the victims
-  int my[kRsSlots], ot[kRsSlots];
+  int my[kRsSlots];
   uint32_t km = 0u;  // bit e: my[e] is untouched
 #pragma unroll
   for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
@@ -280,7 +298,6 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       if (e < Q) {
         const int s = max(my[e], 0);
         fl[e] = flag[s];
-        ot[e] = tag_l[s];
       }
     }
 #pragma unroll
@@ -348,29 +365,31 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     }
     if (bad_vic >= 0) raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)bad_vic);
   }
-  // 4. plan and miss words, then the flag
+  // 4. plan and copy destinations, then the flag
 #pragma unroll
   for (int e = 0; e < kRsPos; ++e) {
     const int j = e * kRsThreads + tid;
-    if (e < P && j < K) put(&plan[j], code[e] >= 0 ? code[e] : -1);
-    const int w = e * kRsWaves + wave;  // word of positions 64 w .. 64 w + 63
-    if (e < P && lane == 0 && w < sc.words) put_word(w, mb[e]);
+    if (e < P && j < K) {
+      const bool miss = (missbits >> e) & 1u;
+      put(&plan[j], code[e] >= 0 ? code[e] : -1);
+      put(&mdst[j], miss && code[e] >= 0 ? code[e] : -1);
+      put(&mslot[j], miss ? vs[e] : -1);
+      if (miss) put(&mold[j], tag_l[vs[e]]);
+    }
   }
   publish();
   // 5. LRU state: the untouched non-victims keep their order at the front,
   //    then the hit and victim slots in ascending slot number, all with
-  //    stamp n; victims lose their old token and take the missed one
+  //    stamp n; victims lose their old token and take the missed one. The
+  //    new order is assembled in LDS (the old one there is no longer read)
+  //    and written out with coalesced 16-byte stores.
   {
     int kpos = kbase;
 #pragma unroll
     for (int e = 0; e < kRsSlots; ++e) {
       if (e < Q) {
         if ((km >> e) & 1u) {
-          if (kpos >= M) {
-            order[kpos - M] = my[e];
-          } else if (ot[e] >= 0 && ot[e] < v.max_context) {
-            rev[ot[e]] = -1;
-          }
+          if (kpos >= M) lru[kpos - M] = my[e];
           ++kpos;
         }
       }
@@ -380,24 +399,50 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     for (int e = 0; e < kRsSlots; ++e) {
       if (e < Q && ((fm >> e) & 1u)) {
         const int s = tid * Q + e;
-        order[fpos++] = s;
-        stamp[s] = n;
+        lru[fpos++] = s;
+        if (!stamp4) stamp[s] = n;
       }
     }
 #pragma unroll
-    for (int e = 0; e < kRsPos; ++e) {
-      if (e < P && ((missbits >> e) & 1u)) {
-        tag[vs[e]] = tok[e];
-        rev[tok[e]] = vs[e];
+    for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+      const int x = tid * Q + 4 * e4;
+      if (4 * e4 < Q && stamp4 && x < S) {
+        int4 w = st4[e4];
+        const uint32_t f = fm >> (4 * e4);
+        w.x = (f & 1u) ? n : w.x;
+        w.y = (f & 2u) ? n : w.y;
+        w.z = (f & 4u) ? n : w.z;
+        w.w = (f & 8u) ? n : w.w;
+        reinterpret_cast<int4*>(stamp)[x >> 2] = w;
       }
     }
+    // (the victims' tags and the reverse map are updated by the copy
+    // workgroups, which hold each miss's token, slot and the slot's old token)
     // page recency for the residency manager: every page the indexer
-    // selected a token of this step takes stamp n
+    // selected a token of this step takes stamp n. With the page table in
+    // LDS (no longer read) the selected pages are marked there and stamped
+    // in one coalesced pass instead of one scattered store per token.
     int32_t* pstamp = v.page_stamp + (size_t)r * v.pages_per_req;
+    constexpr int kTouched = INT32_MIN;
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
-      if (e < P && tok[e] >= 0 && tok[e] < L) pstamp[tok[e] >> lps] = n;
+      if (e < P && tok[e] >= 0 && tok[e] < L) {
+        if (pt_in_lds)
+          ptl[tok[e] >> lps] = kTouched;
+        else
+          pstamp[tok[e] >> lps] = n;
+      }
     }
+    __syncthreads();  // new order and page marks in LDS
+    if ((S & 3) == 0) {
+      for (int x = tid; x < S / 4; x += kRsThreads)
+        reinterpret_cast<int4*>(order)[x] = reinterpret_cast<const int4*>(lru)[x];
+    } else {
+      for (int x = tid; x < S; x += kRsThreads) order[x] = lru[x];
+    }
+    if (pt_in_lds)
+      for (int p = tid; p < npg; p += kRsThreads)
+        if (ptl[p] == kTouched) pstamp[p] = n;
   }
   if (tid == 0) {
     const int n_res = st.n_res, n_hot = st.n_hot;
@@ -406,9 +451,9 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       a.counts_out[3 * i + 1] = n_hot;
       a.counts_out[3 * i + 2] = M;
     }
-    v.counters[3 * r] += n_res;
-    v.counters[3 * r + 1] += n_hot;
-    v.counters[3 * r + 2] += M;
+    v.counters[3 * r] = cnt0[0] + n_res;
+    v.counters[3 * r + 1] = cnt0[1] + n_hot;
+    v.counters[3 * r + 2] = cnt0[2] + M;
     v.step[r] = n;
   }
 }
@@ -416,7 +461,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 // Copy the missed rows of plan positions [c kRsPart, (c + 1) kRsPart) of
 // request i; wave w takes 4 of them.
 template <int ROW_BYTES, bool FP8>
-__device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc, RsStatic& st,
+__device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc,
                                           int i, int c) {
   constexpr int CH = ROW_BYTES / 16;   // 16-byte chunks per row
   constexpr int CPL = (CH + 63) / 64;  // chunks per lane
@@ -457,28 +502,28 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) x[k][u] = s4[lane + 64 * u];
     }
   }
-  // wait for the bookkeeper: poll with device-coherent loads; the plan and
-  // miss words it stored before raising the flag are read the same way
-  if (tid == 0) {
-    int spins = 0;
+  // wait for the bookkeeper (each wave on its own): poll with
+  // device-coherent loads; the copy destinations it stored before raising
+  // the flag are read the same way, one per lane 0..3
+  int spins = 0;
+  if (lane == 0) {
     while (__hip_atomic_load(&sc.flag[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       if (++spins > kSpinLimit) break;
-      __builtin_amdgcn_s_sleep(4);
+      __builtin_amdgcn_s_sleep(1);
     }
-    st.go = spins <= kSpinLimit;
     if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
   }
-  __syncthreads();
-  if (!st.go) return;
-  // (j0 is a multiple of 4, so the 4 bits lie in one mask word)
-  const unsigned long long word = __hip_atomic_load(&sc.miss_mask[(size_t)i * sc.words + (j0 >> 6)],
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned am = (unsigned)((word >> (j0 & 63)) & 0xFull);
-  int32_t* plan = a.plan_out + (size_t)i * K + j0;
+  if (__shfl(spins, 0, 64) > kSpinLimit) return;
+  int md = -1, ms = -1, mo = -1;
+  if (lane < 4 && j0 + lane < K) {
+    const size_t jj = (size_t)i * K + j0 + lane;
+    md = __hip_atomic_load(&sc.mdst[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ms = __hip_atomic_load(&sc.mslot[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mo = ms >= 0 ? __hip_atomic_load(&sc.mold[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  }
   int dsts[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    dsts[k] = ((am >> k) & 1u) ? __hip_atomic_load(&plan[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  for (int k = 0; k < 4; ++k) dsts[k] = __shfl(md, k, 64);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int dst = dsts[k];
@@ -499,9 +544,16 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) d4[lane + 64 * u] = y[u];
     }
   }
-  if (FP8 && lane < 4 && ((am >> lane) & 1u)) {  // one fp8 scale per missed row
-    const int dst = lane == 0 ? dsts[0] : lane == 1 ? dsts[1] : lane == 2 ? dsts[2] : dsts[3];
-    if (dst >= 0) a.pool_scales[dst] = a.host_scales[hbase + t];
+  if (FP8 && lane < 4 && md >= 0) a.pool_scales[md] = a.host_scales[hbase + t];  // one scale per missed row
+  // LRU tables of every miss: the slot's old token leaves the reverse map,
+  // the missed token takes the slot (a missed token is in no slot, so it is
+  // never another miss's old token: these stores do not collide)
+  // (other copy workgroups' guesses may read these entries meanwhile; a
+  // guess only decides which reads start early)
+  if (lane < 4 && ms >= 0) {
+    if (mo >= 0 && mo < v.max_context) v.rev[(size_t)r * v.max_context + mo] = -1;
+    v.slot_tag[(size_t)r * v.hot_rows + ms] = t;
+    v.rev[(size_t)r * v.max_context + t] = ms;
   }
 }
 
@@ -518,7 +570,7 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   } else {
     const int q = role - a.n_req;
     const int i = q / sc.parts, c = q - i * sc.parts;
-    copy_part<ROW_BYTES, FP8>(a, v, sc, st, i, c);
+    copy_part<ROW_BYTES, FP8>(a, v, sc, i, c);
     __syncthreads();
     if (tid == 0 && atomicAdd(&sc.exit_cnt[i], 1u) == (uint32_t)(sc.parts - 1)) {
       sc.flag[i] = 0;  // every copy workgroup of request i has seen the flag
@@ -542,11 +594,12 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
                          int32_t* plan_out, int32_t* counts_out, hipStream_t s) {
   StateView v = make_view(p);
   RsScratch sc;
-  sc.miss_mask = reinterpret_cast<unsigned long long*>(p->state + p->off.rs_miss_mask);
+  sc.mdst = reinterpret_cast<int32_t*>(p->state + p->off.rs_mdst);
+  sc.mslot = reinterpret_cast<int32_t*>(p->state + p->off.rs_mslot);
+  sc.mold = reinterpret_cast<int32_t*>(p->state + p->off.rs_mold);
   sc.flag = reinterpret_cast<uint32_t*>(p->state + p->off.rs_flag);
   sc.exit_cnt = reinterpret_cast<uint32_t*>(p->state + p->off.rs_exit);
   sc.ticket = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);
-  sc.words = (p->d.top_k + 63) / 64;
   sc.parts = (p->d.top_k + kRsPart - 1) / kRsPart;
   RsArgs a{idx, req_ids, n_req,
            pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
