@@ -9,8 +9,9 @@
 //   out = sum_j softmax_j(sm_scale * <q, row_j>) * row_j[0:512]
 //
 // k_attn_mfma (bf16 or fp8 rows, bf16 queries). A workgroup of 8 waves
-// takes 64 query rows (4 blocks of 16) of one request and a contiguous
-// split of its plan, 32 rows (a tile) at a time:
+// takes 64 query rows (4 blocks of 16; or 4 waves and 32 rows when only a
+// few requests are decoded) of one request and a contiguous split of its
+// plan, 32 rows (a tile) at a time:
 //   - rows are fetched straight from the pool into LDS (global_load_lds,
 //     no registers), through a ring of three buffers: tiles t+1 and t+2
 //     are in flight while tile t is computed, and the queries load under
@@ -56,7 +57,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // A workgroup takes QB blocks of 16 query rows with 2 waves per block
-// (launched with QB = 4).
+// (launched with QB = 4, or 2 for a few requests).
 constexpr int kTile = 32;              // rows per tile
 constexpr int kChunks = 2 * kRowDim / 16;        // 72 chunks of 16 B per bf16 row
 constexpr int kRowChunks = kChunks + 1;          // LDS row stride: 73 chunks (one pad chunk)
@@ -85,6 +86,11 @@ __device__ inline u32x2_t tr_load(const uint8_t* p) {
 __device__ inline f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+
+// s_waitcnt immediate: vmcnt(n) (6 bits, split over bits 3:0 and 15:14),
+// expcnt and lgkmcnt left at their maximum (no wait).
+constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 0xF) | ((n & 0x30) << 10); }
+static_assert(vmcnt_imm(0) == 0xF70 && vmcnt_imm(5) == 0xF75 && vmcnt_imm(38) == 0x8F76, "vmcnt encoding");
 
 // Two floats -> one dword of two bf16 made of their upper halves
 // (truncation; exact when the values are representable in bf16).
@@ -224,9 +230,8 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     }
   };
   // vmcnt(n) with expcnt and lgkmcnt left alone (n < 16)
-  constexpr int kWaitOne = 0xF70 | kIssue;      // all but the last tile issued
-  constexpr int kWaitTwo = 0xF70 | 2 * kIssue;  // all but the last two tiles issued
-  static_assert(2 * kIssue < 16, "vmcnt immediate");
+  constexpr int kWaitOne = vmcnt_imm(kIssue);      // all but the last tile issued
+  constexpr int kWaitTwo = vmcnt_imm(2 * kIssue);  // all but the last two tiles issued
 
   // O^T accumulators: block b holds dims 256*half + 16b + 4kg + v (v = 0..3)
   // of query ln
@@ -514,14 +519,19 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   }
   const int n_tiles = (K + kTile - 1) / kTile;
   const uint8_t* zero_row = p->state + p->off.zero_row;
-  constexpr int qb = 4;
-  const int q_per_wg = 16 * qb;
-  const int n_hg = (QR + q_per_wg - 1) / q_per_wg;
   // Split the plan so that about one workgroup per CU is busy, with a floor
   // on the tiles per split so that the fixed cost per workgroup (plan,
-  // queries, partial output) is amortised.
+  // queries, partial output) is amortised. Workgroups take 4 blocks of 16
+  // query rows (8 waves), or 2 blocks (4 waves) when even the smallest
+  // splits of 4-block workgroups leave most CUs idle (a few requests: twice
+  // the workgroups, each with half the LDS traffic per tile).
   static const int forced = env_int("HS_ATTN_TILES_PER_SPLIT", 0);
+  static const int forced_qb = env_int("HS_ATTN_QB", 0);
   constexpr int min_tps = 2;
+  const int64_t wg4 = (int64_t)n_req * ((QR + 63) / 64) * ((n_tiles + min_tps - 1) / min_tps);
+  const int qb = (forced_qb == 2 || forced_qb == 4) ? forced_qb : (wg4 < 256 ? 2 : 4);
+  const int q_per_wg = 16 * qb;
+  const int n_hg = (QR + q_per_wg - 1) / q_per_wg;
   int tps;
   if (forced > 0) {
     tps = forced;
@@ -549,10 +559,14 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
 #define HS_ATTN_LAUNCH(F, B)                                                                                  \
   k_attn_mfma<F, B><<<grid, 128 * (B), 0, s>>>(q16, QR, plan, K, p->pool_rows, sc, p->pool_rows_n, zero_row, c2, \
                                                tps, splits, out, lse_out, part_o, part_lse, err)
-  if (fp8)
-    HS_ATTN_LAUNCH(true, qb);
+  if (fp8 && qb == 4)
+    HS_ATTN_LAUNCH(true, 4);
+  else if (fp8)
+    HS_ATTN_LAUNCH(true, 2);
+  else if (qb == 4)
+    HS_ATTN_LAUNCH(false, 4);
   else
-    HS_ATTN_LAUNCH(false, qb);
+    HS_ATTN_LAUNCH(false, 2);
 #undef HS_ATTN_LAUNCH
   if (splits > 1) {
     const int rows = n_req * QR;
