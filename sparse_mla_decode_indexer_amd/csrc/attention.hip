@@ -210,26 +210,38 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // tile is a constant vmcnt, and the compiler, which counts the same
   // instructions, sees that the tile is complete and adds no wait of its own.
   constexpr int kRowChunksT = FP8 ? kRawChunks : kRowChunks;
-  auto rows_of = [&](int t, int* rr) {
+  // tile-invariant per position: the tile row and the byte offset in the
+  // row (-1: pad chunk or past the tile), from one division, then stepped
+  int rowk[kIssue], coff[kIssue];
+  {
+    int r = tid / kRowChunksT, c = tid - r * kRowChunksT;
+    constexpr int kStepR = kAttThreads / kRowChunksT, kStepC = kAttThreads % kRowChunksT;
 #pragma unroll
     for (int k = 0; k < kIssue; ++k) {
-      const int p = k * kAttThreads + tid;
-      const int r = min(p / kRowChunksT, kTile - 1);
-      rr[k] = t < nt ? prow_s[t * kTile + r] : -1;
+      rowk[k] = min(r, kTile - 1);
+      coff[k] = (r < kTile && (FP8 || c < kChunks)) ? c * 16 : -1;
+      c += kStepC;
+      r += kStepR;
+      if (c >= kRowChunksT) {
+        c -= kRowChunksT;
+        ++r;
+      }
     }
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  auto rows_of = [&](int t, int* rr) {
+#pragma unroll
+    for (int k = 0; k < kIssue; ++k) rr[k] = t < nt ? prow_s[t * kTile + rowk[k]] : -1;
   };
   auto issue = [&](const int* rr, uint8_t* dst) {
 #pragma unroll
     for (int k = 0; k < kIssue; ++k) {
-      const int p = k * kAttThreads + tid;
-      const int r = p / kRowChunksT, c = p - r * kRowChunksT;  // c <= 72
-      const bool real = rr[k] >= 0 && p < kPos && (FP8 || c < kChunks);
-      const size_t rb = FP8 ? kRowDim : 2 * kRowDim;
-      const uint8_t* src = real ? pool + (size_t)rr[k] * rb + c * 16 : zero_row + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave * 64) * 16), 16, 0, 0);
+      constexpr size_t rb = FP8 ? kRowDim : 2 * kRowDim;
+      const bool real = (rr[k] | coff[k]) >= 0;
+      const uint8_t* src = real ? pool + (size_t)rr[k] * rb + coff[k] : zero_row;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave_s * 64) * 16), 16, 0, 0);
     }
   };
-  // vmcnt(n) with expcnt and lgkmcnt left alone (n < 16)
   constexpr int kWaitOne = vmcnt_imm(kIssue);      // all but the last tile issued
   constexpr int kWaitTwo = vmcnt_imm(2 * kIssue);  // all but the last two tiles issued
 
@@ -388,8 +400,11 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 }
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
-// Thread (row, 4 dims): all of its partial loads are in flight together.
+// Thread (row, 4 dims): kBatch partial loads are in flight together; kBatch
+// is the power of two >= the split count (at most 32), so one round trip
+// covers the usual split counts without many padding loads.
 constexpr int kCombineThreads = 256;
+template <int kBatch>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, int QR, int n_splits,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_lse,
@@ -405,13 +420,12 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
   float M = -INFINITY;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.f;
-  constexpr int kBatch = 16;  // partial loads in flight per thread
   for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
     float w[kBatch];
     float4 x[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int s = min(s0 + u, n_splits - 1);
+      const int s = min(s0 + u, n_splits - 1);  // padding entries reload the last split
       const size_t pr = base + (size_t)s * QR;
       w[u] = s0 + u < n_splits ? part_lse[pr] : -INFINITY;
       x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
@@ -571,8 +585,17 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   if (splits > 1) {
     const int rows = n_req * QR;
     const int64_t threads = (int64_t)rows * (kNope / 4);
-    k_attn_combine<<<(int)((threads + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
-        rows, QR, splits, part_o, part_lse, out, lse_out);
+    const int nb = (int)((threads + kCombineThreads - 1) / kCombineThreads);
+#define HS_COMBINE(B) k_attn_combine<B><<<nb, kCombineThreads, 0, s>>>(rows, QR, splits, part_o, part_lse, out, lse_out)
+    if (splits <= 4)
+      HS_COMBINE(4);
+    else if (splits <= 8)
+      HS_COMBINE(8);
+    else if (splits <= 16)
+      HS_COMBINE(16);
+    else
+      HS_COMBINE(32);
+#undef HS_COMBINE
   }
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
