@@ -565,22 +565,31 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   if (tid == 0) st.role = (int)atomicAdd(&sc.ticket[0], 1u);
   __syncthreads();
   const int role = st.role;
+  int i = -1;  // request of a copy workgroup
   if (role < a.n_req) {
     bookkeep(a, v, sc, st, rs_dyn, role);
   } else {
     const int q = role - a.n_req;
-    const int i = q / sc.parts, c = q - i * sc.parts;
-    copy_part<ROW_BYTES, FP8>(a, v, sc, i, c);
-    __syncthreads();
-    if (tid == 0 && atomicAdd(&sc.exit_cnt[i], 1u) == (uint32_t)(sc.parts - 1)) {
-      sc.flag[i] = 0;  // every copy workgroup of request i has seen the flag
-      sc.exit_cnt[i] = 0;
-    }
+    i = q / sc.parts;
+    copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts);
   }
   __syncthreads();
-  if (tid == 0 && atomicAdd(&sc.ticket[1], 1u) == gridDim.x - 1) {
-    sc.ticket[0] = 0;  // every workgroup has taken its role
-    sc.ticket[1] = 0;
+  // Exit counts, both in one round trip: the last copy workgroup of request
+  // i (all of them have seen its flag) clears the flag; the last workgroup
+  // of the grid (all have taken their roles) clears the tickets. The
+  // clears only matter to the next launch.
+  if (tid == 0) {
+    uint32_t* ec = &sc.exit_cnt[i >= 0 ? i : 0];
+    const uint32_t e = __hip_atomic_fetch_add(ec, i >= 0 ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t x = __hip_atomic_fetch_add(&sc.ticket[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i >= 0 && e == (uint32_t)(sc.parts - 1)) {
+      sc.flag[i] = 0;
+      sc.exit_cnt[i] = 0;
+    }
+    if (x == gridDim.x - 1) {
+      sc.ticket[0] = 0;
+      sc.ticket[1] = 0;
+    }
   }
 }
 
