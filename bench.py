@@ -249,7 +249,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "requests": R, "context": int(lens.max()),
                    "kv_dtype": spec.kv_dtype, "heads": spec.heads, "q_per_req": spec.q_per_req,
-                   "top_k": Kt, "hot_rows": S, "residency": spec.residency},
+                   "top_k": Kt, "hot_rows": S, "residency": spec.residency,
+                   **({"layers": spec.layers} if spec.layers > 1 else {})},
+        **({"layer_steps_per_s": round(value * spec.layers, 1)} if spec.layers > 1 else {}),
         "rows_resolved_per_s": round(rows_per_step * value, 1),
         "misses_per_step": round(float(misses_per_step), 1),
         "hits_per_step": round(float(dc[1] / K), 1),

@@ -15,6 +15,18 @@
  * host store ahead of need and, under a GPU page budget, moves a request's
  * coldest pages back to host memory.
  *
+ * Multi-layer steps ([P2] §"关键架构细节", lightweight execution: the
+ * sparse-MLA work of all layers is issued once per step, in the model's
+ * stream order). A request slot is the unit of state (page table, hot
+ * buffer, LRU state, top-K bound), so one pool holds the slots of every
+ * (layer, request) pair — numbered layer-major, slot = layer * R + r — with
+ * their rows in the shared page pool and host store, as the hot buffers are
+ * ordinary blocks leased from one shared pool. One call of each per-step
+ * entry point with req_ids listing the slots of every layer then selects,
+ * resolves and attends all layers in one launch per stage; inputs and
+ * outputs are indexed by position in req_ids (scores [n][stride], queries
+ * [n][Q][H][576], plans [n][K], outputs [n][Q][H][512]).
+ *
  * Pages describing the method (cited by title and section):
  *   [P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" (agentlenshq.com)
  *   [P3] "vLLM Hybrid HiSparse：稀疏MLA破解长上下文显存瓶颈" (kongchang.com)

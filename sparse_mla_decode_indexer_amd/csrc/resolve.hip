@@ -502,6 +502,9 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) x[k][u] = s4[lane + 64 * u];
     }
   }
+  // the fp8 scale of a guessed miss is read with its row (lane k: position k)
+  float scale = 0.f;
+  if (FP8 && guess) scale = a.host_scales[hbase + t];
   // wait for the bookkeeper (each wave on its own): poll with
   // device-coherent loads; the copy destinations it stored before raising
   // the flag are read the same way, one per lane 0..3
@@ -544,7 +547,8 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) d4[lane + 64 * u] = y[u];
     }
   }
-  if (FP8 && lane < 4 && md >= 0) a.pool_scales[md] = a.host_scales[hbase + t];  // one scale per missed row
+  if (FP8 && lane < 4 && md >= 0)  // one scale per missed row (read now if not guessed)
+    a.pool_scales[md] = guess ? scale : a.host_scales[hbase + t];
   // LRU tables of every miss: the slot's old token leaves the reverse map,
   // the missed token takes the slot (a missed token is in no slot, so it is
   // never another miss's old token: these stores do not collide)

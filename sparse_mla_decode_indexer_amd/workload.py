@@ -18,7 +18,7 @@ Shapes follow the pages' description of the method:
     benchmarking").
 
 Recipe (all draws seeded; every array is produced once on the host):
-  * master seed = 20261202 + c for workload c in 1..5;
+  * master seed = 20261202 + c for workload c in 1..6;
     ``numpy.random.SeedSequence(seed).spawn(6)`` gives independent streams
     for scores, rows, queries, page placement, context lengths and topic
     shifts; the rows stream is split again per request and per chunk of
@@ -79,6 +79,11 @@ class WorkloadSpec:
     growth: Optional[Tuple[int, int, int, int]] = None  # first, later, out, turns
     gpu_token_budget: Optional[int] = None  # newest tokens on GPU per request
     page_size: int = PAGE_SIZE
+    # Multi-layer step: n_req counts request slots, layer-major (slot =
+    # layer * n_req // layers + request); every slot has its own rows, page
+    # table, hot buffer, scores and queries, and the slots of one request
+    # share its context length.
+    layers: int = 1
 
     @property
     def seed(self) -> int:
@@ -109,6 +114,14 @@ SPECS: Dict[str, WorkloadSpec] = {
         name="agent16", index=5, n_req=16, kv_dtype=KV_FP8, q_dtype="bf16",
         heads=128, q_per_req=4, top_k=2048, hot_rows=4096, steps=715,
         residency="budget", gpu_token_budget=145408, growth=(74160, 753, 220, 13),
+        scores=("ar1", 0.9)),
+    # Multi-layer step: the sparse-MLA work of 16 layers of one 128K-token
+    # request (fp8 rows, 75% of each layer's pages on the host) in one call
+    # of each entry point.
+    "layers16-128k-fp8": WorkloadSpec(
+        name="layers16-128k-fp8", index=6, n_req=16, layers=16, ctx=131072,
+        kv_dtype=KV_FP8, q_dtype="bf16", heads=128, q_per_req=1, top_k=2048,
+        hot_rows=4096, steps=32, residency="oldest_host", host_pages=1536,
         scores=("ar1", 0.9)),
     # Aggregate reading of the 142K admission limit: 9,088 newest tokens
     # (142 pages) of each of the 16 requests stay on GPU.
@@ -243,9 +256,12 @@ def generate(spec: WorkloadSpec) -> Workload:
     gens = {k: np.random.Generator(np.random.PCG64(s)) for k, s in
             zip(("scores", "rows", "queries", "pages", "contexts", "shifts"), ss)}
     R = spec.n_req
+    if spec.n_req % spec.layers:
+        raise ValueError("n_req must be a multiple of layers")
     if spec.ctx_range is not None:
         lo, hi = spec.ctx_range
-        ctx0 = gens["contexts"].integers(lo, hi, endpoint=True, size=R).astype(np.int64)
+        per = gens["contexts"].integers(lo, hi, endpoint=True, size=R // spec.layers).astype(np.int64)
+        ctx0 = np.tile(per, spec.layers)
     elif spec.growth is not None:
         ctx0 = np.full(R, spec.growth[0], dtype=np.int64)
     else:

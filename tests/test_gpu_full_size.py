@@ -26,6 +26,7 @@ FULL = [
     ("single-1m-fp8", 8, [5, 100]),  # the score stream redraws every score at step 3
     ("agent16", 6, [3, 64]),
     ("agent16-b", 6, [3, 64]),
+    ("layers16-128k-fp8", 3, [0, 127]),
 ]
 
 

@@ -52,6 +52,13 @@ def test_agent_q4_fp8_growing():
     run_steps(spec, 12)
 
 
+def test_multi_layer_step():
+    """Four layers of two requests in one call of each entry point (layer-
+    major slots, each with its own rows, scores, queries, page table and hot
+    buffer): every slot bit-exact / within the bar, as a batch would be."""
+    run_steps(small("layers16-128k-fp8", n_req=8, layers=4, ctx=16384, host_pages=192), 4, heads=[0, 127])
+
+
 def test_small_page_and_min_hot_buffer():
     # page size 16, S == K: every miss must reuse an untouched slot
     spec = small("single-128k", ctx=6000, host_pages=280, page_size=16, top_k=256, hot_rows=256)

@@ -2,6 +2,7 @@
 import dataclasses
 
 import numpy as np
+import pytest
 
 from sparse_mla_decode_indexer_amd import workload as W
 
@@ -71,3 +72,16 @@ def test_agent_schedule():
     assert sched[55, 0] == 74160 + 220 + 753
     assert sched[-1, 0] == 86056 - 4
     assert W.final_context(W.SPECS["agent16"], np.array([74160]))[0] == 86056
+
+
+def test_multi_layer_slots_share_contexts():
+    """Multi-layer specs: slots are layer-major and the slots of one request
+    share its context length; each slot still draws its own rows."""
+    spec = small("batch32", n_req=6, layers=3, ctx_range=(3000, 9000), steps=1)
+    wl = W.generate(spec)
+    per = wl.ctx0.reshape(3, 2)
+    assert (per == per[0]).all() and per[0, 0] != per[0, 1]
+    a, b = wl.host_base[0], wl.host_base[2]  # request 0 in layers 0 and 1
+    assert not np.array_equal(wl.rows[a:a + 64], wl.rows[b:b + 64])
+    with pytest.raises(ValueError):
+        W.generate(small("batch32", n_req=5, layers=3, ctx_range=(3000, 9000), steps=1))
