@@ -9,18 +9,19 @@
 //   bookkeeper (tickets 0 .. n_req-1), one per request: classifies the K
 //     tokens (resident > hot > miss), stamps the hit slots, picks the victims
 //     and rewrites the LRU order with ordered compactions in LDS, writes the
-//     plan, the copy destination, hot slot and that slot's old token of
-//     every missed position and the counts, and publishes the plan with a
-//     per-request flag;
+//     plan and the counts, and for every plan position the hot slot and that
+//     slot's old token (misses) and last the copy destination: the pool row
+//     a miss is copied to, or -1;
 //   copy workgroup (request i, part c), one per 64 plan positions (4 per
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
-//     store over PCIe right away; each wave then waits for the flag and
-//     writes the rows the bookkeeper actually classified as misses into
-//     their hot slots (rows it did not guess are read then), and moves the
-//     slots' tags and reverse-map entries from the old tokens to the new. The guess only decides
-//     how early the PCIe reads start; which rows are written comes from the
-//     bookkeeper.
+//     store over PCIe right away; each wave then waits until its four copy
+//     destinations are published, writes the rows the bookkeeper actually
+//     classified as misses into their hot slots (rows it did not guess are
+//     read then), moves the slots' tags and reverse-map entries from the old
+//     tokens to the new, and puts its destination entries back to "pending"
+//     for the next call. The guess only decides how early the PCIe reads
+//     start; which rows are written comes from the bookkeeper.
 // Bookkeeper thread t owns plan positions t + 1024 e (e < P), so wave w
 // holds plan positions 1024 e + 64 w .. + 63 and the token-order rank of a
 // miss comes from a ballot and per-wave counts. It owns
@@ -31,7 +32,8 @@
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
 // bounded (a device error is raised past the bound and the copy skipped).
-// Counters and flags are left cleared for the next call.
+// The destination entries start "pending" (pool initialisation) and are
+// left pending by their copy wave; the role tickets are left cleared.
 //
 // LRU order. lru_order lists all S slots in ascending (stamp, slot). With U
 // the slots hit this step and M misses, the victims are the first M slots of
@@ -53,8 +55,6 @@ struct RsScratch {
   int32_t* mdst;                  // [batch][K] pool row a missed position is copied to, else -1
   int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
   int32_t* mold;                  // [batch][K] token that slot held before (or -1)
-  uint32_t* flag;                 // [batch] 1 once request i's plan is published
-  uint32_t* exit_cnt;             // [batch] copy workgroups of request i done
   uint32_t* ticket;               // [2] roles handed out, workgroups exited
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
@@ -64,7 +64,8 @@ constexpr int kRsWaves = kRsThreads / 64;
 constexpr int kRsPos = kMaxTopK / kRsThreads;      // plan positions per bookkeeper thread, at most
 constexpr int kRsSlots = kMaxHotRows / kRsThreads;  // LRU positions per bookkeeper thread, at most
 constexpr int kRsPart = 4 * kRsWaves;              // plan positions per copy workgroup
-constexpr int kSpinLimit = 1 << 20;                // polls of the flag (>= 0.1 s) before giving up
+constexpr int kSpinLimit = 1 << 20;                // polls of a destination (>= 0.1 s) before giving up
+constexpr int32_t kRsPending = INT32_MIN;          // copy destination not yet published
 
 struct RsArgs {
   const int32_t* idx;
@@ -110,20 +111,19 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   const int32_t* sel = a.idx + (size_t)i * K;
   int32_t* plan = a.plan_out + (size_t)i * K;
   const int r0 = a.req_ids[i];
-  // What the copy workgroups read (plan, copy destinations, flag) is written with
-  // device-coherent stores; the flag goes out once this workgroup's stores
-  // of the rest have completed. The LRU state is written afterwards: no copy
-  // workgroup reads it, and the flag does not wait for it.
+  // What the copy workgroups read (slot, old token, destination) is written
+  // with device-coherent stores; a position's destination goes out (from
+  // the thread that owns the position) once that thread's other stores have
+  // completed, so a copy wave that sees it also sees the rest. The LRU
+  // state is written afterwards: no copy workgroup reads it.
   auto put = [](int32_t* p, int x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   int32_t* mdst = sc.mdst + (size_t)i * K;
   int32_t* mslot = sc.mslot + (size_t)i * K;
   int32_t* mold = sc.mold + (size_t)i * K;
-  auto publish = [&]() {
+  auto stores_done = []() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
     asm volatile("" ::: "memory");
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&sc.flag[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if (r0 < 0 || r0 >= v.max_requests) {
     if (tid == 0) {
@@ -132,10 +132,10 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     }
     for (int j = tid; j < K; j += kRsThreads) {
       put(&plan[j], -1);
-      put(&mdst[j], -1);
       put(&mslot[j], -1);
     }
-    publish();
+    stores_done();
+    for (int j = tid; j < K; j += kRsThreads) put(&mdst[j], -1);
     return;
   }
   const int r = r0;
@@ -365,19 +365,23 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     }
     if (bad_vic >= 0) raise_error(v.error, HS_DEV_PAGE_RANGE, (uint32_t)r, (uint32_t)bad_vic);
   }
-  // 4. plan and copy destinations, then the flag
+  // 4. plan, slots and old tokens, then the copy destinations
 #pragma unroll
   for (int e = 0; e < kRsPos; ++e) {
     const int j = e * kRsThreads + tid;
     if (e < P && j < K) {
       const bool miss = (missbits >> e) & 1u;
       put(&plan[j], code[e] >= 0 ? code[e] : -1);
-      put(&mdst[j], miss && code[e] >= 0 ? code[e] : -1);
       put(&mslot[j], miss ? vs[e] : -1);
       if (miss) put(&mold[j], tag_l[vs[e]]);
     }
   }
-  publish();
+  stores_done();
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) {
+    const int j = e * kRsThreads + tid;
+    if (e < P && j < K) put(&mdst[j], ((missbits >> e) & 1u) && code[e] >= 0 ? code[e] : -1);
+  }
   // 5. LRU state: the untouched non-victims keep their order at the front,
   //    then the hit and victim slots in ascending slot number, all with
   //    stamp n; victims lose their old token and take the missed one. The
@@ -505,24 +509,31 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   // the fp8 scale of a guessed miss is read with its row (lane k: position k)
   float scale = 0.f;
   if (FP8 && guess) scale = a.host_scales[hbase + t];
-  // wait for the bookkeeper (each wave on its own): poll with
-  // device-coherent loads; the copy destinations it stored before raising
-  // the flag are read the same way, one per lane 0..3
+  // wait for the bookkeeper (each wave on its own): lanes 0..3 poll their
+  // positions' destinations with device-coherent loads until none is
+  // pending, then put them back to pending for the next call
+  const bool mine = lane < 4 && j0 + lane < K;
+  const size_t jj = (size_t)i * K + j0 + (lane & 3);
+  int md = -1;
   int spins = 0;
-  if (lane == 0) {
-    while (__hip_atomic_load(&sc.flag[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (++spins > kSpinLimit) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
+  for (;;) {
+    if (mine) md = __hip_atomic_load(&sc.mdst[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!__any(mine && md == kRsPending)) break;  // (loop condition uniform per wave)
+    if (++spins > kSpinLimit) break;
+    __builtin_amdgcn_s_sleep(1);
   }
-  if (__shfl(spins, 0, 64) > kSpinLimit) return;
-  int md = -1, ms = -1, mo = -1;
-  if (lane < 4 && j0 + lane < K) {
-    const size_t jj = (size_t)i * K + j0 + lane;
-    md = __hip_atomic_load(&sc.mdst[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ms = __hip_atomic_load(&sc.mslot[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    mo = ms >= 0 ? __hip_atomic_load(&sc.mold[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  if (spins > kSpinLimit) {  // (leave every entry pending, published or not)
+    if (mine) __hip_atomic_store(&sc.mdst[jj], kRsPending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
+    return;
+  }
+  int ms = -1, mo = -1;
+  if (mine) {
+    __hip_atomic_store(&sc.mdst[jj], kRsPending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (md >= 0) {
+      ms = __hip_atomic_load(&sc.mslot[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mo = __hip_atomic_load(&sc.mold[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   int dsts[4];
 #pragma unroll
@@ -569,31 +580,18 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   if (tid == 0) st.role = (int)atomicAdd(&sc.ticket[0], 1u);
   __syncthreads();
   const int role = st.role;
-  int i = -1;  // request of a copy workgroup
   if (role < a.n_req) {
     bookkeep(a, v, sc, st, rs_dyn, role);
   } else {
     const int q = role - a.n_req;
-    i = q / sc.parts;
+    const int i = q / sc.parts;
     copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts);
   }
-  __syncthreads();
-  // Exit counts, both in one round trip: the last copy workgroup of request
-  // i (all of them have seen its flag) clears the flag; the last workgroup
-  // of the grid (all have taken their roles) clears the tickets. The
-  // clears only matter to the next launch.
-  if (tid == 0) {
-    uint32_t* ec = &sc.exit_cnt[i >= 0 ? i : 0];
-    const uint32_t e = __hip_atomic_fetch_add(ec, i >= 0 ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t x = __hip_atomic_fetch_add(&sc.ticket[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (i >= 0 && e == (uint32_t)(sc.parts - 1)) {
-      sc.flag[i] = 0;
-      sc.exit_cnt[i] = 0;
-    }
-    if (x == gridDim.x - 1) {
-      sc.ticket[0] = 0;
-      sc.ticket[1] = 0;
-    }
+  // the last workgroup of the grid (all have taken their roles) clears the
+  // tickets for the next launch
+  if (tid == 0 && atomicAdd(&sc.ticket[1], 1u) == gridDim.x - 1) {
+    sc.ticket[0] = 0;
+    sc.ticket[1] = 0;
   }
 }
 
@@ -610,8 +608,6 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   sc.mdst = reinterpret_cast<int32_t*>(p->state + p->off.rs_mdst);
   sc.mslot = reinterpret_cast<int32_t*>(p->state + p->off.rs_mslot);
   sc.mold = reinterpret_cast<int32_t*>(p->state + p->off.rs_mold);
-  sc.flag = reinterpret_cast<uint32_t*>(p->state + p->off.rs_flag);
-  sc.exit_cnt = reinterpret_cast<uint32_t*>(p->state + p->off.rs_exit);
   sc.ticket = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);
   sc.parts = (p->d.top_k + kRsPart - 1) / kRsPart;
   RsArgs a{idx, req_ids, n_req,
