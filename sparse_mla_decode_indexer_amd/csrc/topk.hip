@@ -231,6 +231,22 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   const uint32_t* cmx = sc.maxk + (size_t)i * sc.max_chunks;
   const uint32_t thr = sc.bound[r];
 
+  // Speculative preload (contexts of up to NW * kPreSlots chunks): the
+  // first 64 * kPreU survivors of each of this wave's chunks (chunks wave,
+  // wave + NW, ...), issued with the chunk counts so that both arrive in one
+  // round trip; entries past a chunk's count are never used.
+  constexpr int kPreSlots = 4, kPreU = 2;
+  const bool preload = nch <= NW * kPreSlots;
+  uint2 pv[kPreSlots][kPreU];
+  if (preload) {
+#pragma unroll
+    for (int q = 0; q < kPreSlots; ++q) {
+      const int c = min(wave + NW * q, nch - 1);
+#pragma unroll
+      for (int u = 0; u < kPreU; ++u) pv[q][u] = cand[(size_t)c * kTkChunk + lane + 64 * u];
+    }
+  }
+
   // 1. chunk offsets of the survivors, their count and largest key
   for (int b = tid; b < 3 * kTkBins; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
   int run = 0;
@@ -369,7 +385,28 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   };
 
   // 2. first digit (bits s1 .. B-1 of key - base), staging into LDS on the way
-  if (staged && !narrowed) {
+  if (staged && !narrowed && preload) {  // from the preloaded registers, chunk by chunk
+#pragma unroll
+    for (int q = 0; q < kPreSlots; ++q) {
+      const int c = wave + NW * q;
+      if (c < nch) {  // uniform per wave
+        const int o = off[c], m = off[c + 1] - o;
+#pragma unroll
+        for (int u = 0; u < kPreU; ++u) {
+          const int j = lane + 64 * u;
+          if (j < m) {
+            surv[o + j] = pv[q][u];
+            atomicAdd(&hist[0][(pv[q][u].x - base) >> s1], 1u);
+          }
+        }
+        for (int j = 64 * kPreU + lane; j < m; j += 64) {  // (a chunk with more survivors)
+          const uint2 e = cand[(size_t)c * kTkChunk + j];
+          surv[o + j] = e;
+          atomicAdd(&hist[0][(e.x - base) >> s1], 1u);
+        }
+      }
+    }
+  } else if (staged && !narrowed) {
     constexpr int U = 4;
     for (int x0 = tid; x0 < n; x0 += U * kTkSelThreads) {
       uint2 e[U];
