@@ -340,3 +340,27 @@ def test_attention_score_jumps(kv, shape):
         assert pool.device_error()[0] == 0
     finally:
         pool.close()
+
+
+def test_imported_prefix_start_shared_host_rows():
+    """None-resident start from an imported prefix ([P2] residency state 3,
+    and P/D imports landing host-side): request 1 reuses request 0's prefix,
+    which exists only in the host store (its page table is all placeholders,
+    its hot buffer empty), while request 0 keeps its newest pages on the GPU.
+    The prefix rows land in the host store after both requests are set up.
+    Both requests read the same host rows; every step is checked as in the
+    other parity tests."""
+    spec = small("single-128k", n_req=2, ctx=16384, host_pages=160, steps=6)
+    wl = W.generate(spec)
+    wl.gpu_page[1][:] = -1                  # request 1: placeholders only
+    wl.host_base[1] = wl.host_base[0]       # ... over request 0's imported rows
+    rn = Runner(wl)
+    try:
+        a, n = int(wl.host_base[0]), int(wl.ctx0[0])
+        rn.pool.host_store[a:a + n] = 0xFF  # the import has not landed yet
+        rn.pool.host_store[a:a + n] = rn.raw[a:a + n]  # ... now it has
+        for _ in range(spec.steps):
+            ref = rn.step(heads=[0, 127])
+        assert np.asarray(ref["counts"])[1][0] == 0  # request 1 never reads a resident row
+    finally:
+        rn.close()
