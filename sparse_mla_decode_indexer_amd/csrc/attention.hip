@@ -392,11 +392,13 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     dst = part_o + prow * kNope;
     if (kg == 0 && half == 0) part_lse[prow] = lse2;
   }
-  // lane holds dims 256*half + 16b + 4kg + v, v = 0..3
+  // lane holds dims 256*half + 16b + 4kg + v, v = 0..3; streaming stores
+  // (read once, by the merge kernel or the caller): fewer dirty L2 lines to
+  // write back when the kernel ends
 #pragma unroll
   for (int b = 0; b < 16; ++b)
-    *reinterpret_cast<float4*>(dst + 256 * half + 16 * b + 4 * kg) =
-        make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv);
+    __builtin_nontemporal_store(f32x4_t{acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv},
+                                reinterpret_cast<f32x4_t*>(dst + 256 * half + 16 * b + 4 * kg));
 }
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
@@ -428,7 +430,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
       const int s = min(s0 + u, n_splits - 1);  // padding entries reload the last split
       const size_t pr = base + (size_t)s * QR;
       w[u] = s0 + u < n_splits ? part_lse[pr] : -INFINITY;
-      x[u] = reinterpret_cast<const float4*>(part_o + pr * kNope)[d4];
+      const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(part_o + pr * kNope) + d4);
+      x[u] = make_float4(t[0], t[1], t[2], t[3]);  // (read once: streaming load)
     }
     float mb = M;
 #pragma unroll
@@ -446,7 +449,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  reinterpret_cast<float4*>(out + (size_t)row * kNope)[d4] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  __builtin_nontemporal_store(f32x4_t{o.x * inv, o.y * inv, o.z * inv, o.w * inv},
+                              reinterpret_cast<f32x4_t*>(out + (size_t)row * kNope) + d4);
   if (lse_out && d4 == 0) lse_out[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 

@@ -546,7 +546,7 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
     if ((gb >> k) & 1u) {
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) d4[lane + 64 * u] = x[k][u];
+        if (lane + 64 * u < CH) __builtin_nontemporal_store(x[k][u], d4 + lane + 64 * u);  // (streaming)
     } else {  // a miss that was not guessed (rare): read it now
       const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * ROW_BYTES);
       u32x4 y[CPL];
@@ -555,7 +555,7 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
         if (lane + 64 * u < CH) y[u] = s4[lane + 64 * u];
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) d4[lane + 64 * u] = y[u];
+        if (lane + 64 * u < CH) __builtin_nontemporal_store(y[u], d4 + lane + 64 * u);
     }
   }
   if (FP8 && lane < 4 && md >= 0)  // one scale per missed row (read now if not guessed)
