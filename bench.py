@@ -335,41 +335,50 @@ def timed_entry_points(pool, buf, steps):
 
 def residency_probe(pool, buf, spec, pages_per_call: int = 64, calls: int = 4):
     """Residency manager on the benchmark's pool after the timed steps (not
-    part of a decode step): proactive copies of `pages_per_call` complete GPU
-    pages per call into the pinned host store (PCIe device-to-host writes),
-    then one release call under a budget of half the GPU pages. HIP events on
-    the stream the kernel runs on."""
+    part of a decode step): `calls` proactive-copy calls of `pages_per_call`
+    complete GPU pages each into the pinned host store (PCIe device-to-host
+    writes), enqueued back to back, then one release call under a budget of
+    half the GPU pages. HIP events on the stream the kernels run on; a large
+    device fill is enqueued first so that the host has queued the calls
+    before the first event is reached and the events time GPU work only."""
     import torch
     R = spec.n_req
     dev = buf.req_ids.device
-    counts = torch.zeros(R, 2, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    copy_ms, copied = 0.0, 0
-    for _ in range(calls):
+    filler = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
+
+    def timed(fn):
+        filler.fill_(1.0)  # keeps the GPU busy while the host enqueues fn's launches
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        pool.update_residency(buf.req_ids, None, pages_per_call, 0, None, counts)
+        fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        copy_ms += e0.elapsed_time(e1)
-        copied += int(counts[:, 0].sum().item())
+        return e0.elapsed_time(e1)
+
+    cnts = [torch.zeros(R, 2, dtype=torch.int32, device=dev) for _ in range(calls)]
+
+    def copies():
+        for c in cnts:
+            pool.update_residency(buf.req_ids, None, pages_per_call, 0, None, c)
+
+    copy_ms = timed(copies)
+    copied = int(sum(int(c[:, 0].sum().item()) for c in cnts))
     pt = pool.state_views()["page_table"]
     held = int((pt[:R] >= 0).sum().item())
     budget = torch.full((R,), max(held // (2 * R), 0), dtype=torch.int32, device=dev)
     freed = torch.empty(R, 1024, dtype=torch.int32, device=dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    pool.update_residency(buf.req_ids, budget, 0, 1024, freed, counts)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    counts = torch.zeros(R, 2, dtype=torch.int32, device=dev)
+    rel_ms = timed(lambda: pool.update_residency(buf.req_ids, budget, 0, 1024, freed, counts))
     released = int(counts[:, 1].sum().item())
+    del filler
     row_bytes = pool.row_bytes + (4 if spec.kv_dtype == "fp8" else 0)
     copied_bytes = copied * spec.page_size * row_bytes
     gbs = copied_bytes / (copy_ms * 1e-3) / 1e9 if copied else 0.0
     return {"calls": calls, "copied_pages": copied, "copied_bytes": copied_bytes,
             "copy_call_us": round(copy_ms * 1e3 / calls, 2), "copy_gbs": round(gbs, 2),
             "pcie_peak_gbs": PCIE_PEAK_GBS, "copy_frac": round(gbs / PCIE_PEAK_GBS, 4),
-            "release_call_us": round(e0.elapsed_time(e1) * 1e3, 2), "released_pages": released}
+            "release_call_us": round(rel_ms * 1e3, 2), "released_pages": released}
 
 
 def cpu_baseline(wl, host_scores, host_q, sched, budget_s):

@@ -39,6 +39,7 @@ struct Offsets {
   size_t zero_row;  // kRowDim * 4 bytes of zeros, never written after init
   size_t tk_count, tk_max, tk_cand, tk_bound;
   size_t rs_mdst, rs_mslot, rs_mold, rs_ticket;
+  size_t ru_list, ru_ncopy;  // residency manager: pages to copy [B][kRuMaxList][2], their count [B]
   size_t at_part_o, at_part_lse;
   int64_t at_part_rows;  // capacity of partial rows
 };

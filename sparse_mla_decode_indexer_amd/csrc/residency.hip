@@ -9,9 +9,10 @@
 // k_update_residency: one 1,024-thread workgroup per request.
 //   1. One ordered pass over the request's pages counts its GPU pages and
 //      lists, in page order, the complete GPU pages without a host copy; the
-//      first max_copy of them are copied (rows and fp8 scales) from the pool
-//      into the mapped host store, 16 bytes per thread and access, and marked
-//      host-valid. Because the copies take the lowest pending pages, a
+//      first max_copy of them are marked host-valid and written to a list
+//      that k_residency_copy then copies (rows and fp8 scales) from the pool
+//      into the mapped host store with many workgroups, 16 bytes per thread
+//      and access. Because the copies take the lowest pending pages, a
 //      pending page counts as copied exactly when it is not above the last
 //      listed one.
 //   2. If the request holds more GPU pages than its budget, d = min(excess,
@@ -25,6 +26,8 @@
 // token of the page) and by set_residency (the step at which a page entered
 // the context).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "hs_internal.h"
 
@@ -43,6 +46,8 @@ struct RuArgs {
   int row_bytes;
   int32_t* freed_out;   // [n_req][max_demote] or null
   int32_t* counts_out;  // [n_req][2] or null
+  int32_t* list;        // [n_req][kRuMaxList][2] pages to copy: (logical page, pool page)
+  int32_t* ncopy;       // [n_req] entries of list
 };
 
 __device__ inline int ru_wave_incl_sum(int x) {
@@ -107,12 +112,11 @@ __global__ __launch_bounds__(kRuThreads) void k_update_residency(RuArgs a, State
     }
     return;
   }
-  const int L = v.ctx_len[r], ps = v.page_size, lps = v.log2_ps;
+  const int L = v.ctx_len[r], ps = v.page_size;
   const int npg = (L + ps - 1) / ps, full = L / ps;
   int32_t* pt = v.page_table + (size_t)r * v.pages_per_req;
   const int32_t* st = v.page_stamp + (size_t)r * v.pages_per_req;
   uint8_t* hv = v.host_valid + (size_t)r * v.pages_per_req;
-  const int64_t hbase = v.host_base[r];
 
   // 1. GPU pages held, pending copies (in page order), demotion candidates
   int pend_total = 0, my_gpu = 0;
@@ -140,25 +144,12 @@ __global__ __launch_bounds__(kRuThreads) void k_update_residency(RuArgs a, State
     return ok;
   };
 
-  // copy the listed pages into the host store
-  {
-    const int CH = a.row_bytes / 16;
-    const int per_page = ps * CH;
-    const int total = ncopy * per_page;
-    for (int x = tid; x < total; x += kRuThreads) {
-      const int k = x / per_page, rem = x - k * per_page;
-      const int o = rem / CH, c = rem - o * CH;
-      const ru_u32x4* src = reinterpret_cast<const ru_u32x4*>(
-          a.pool_rows + ((int64_t)list_g[k] * ps + o) * a.row_bytes) + c;
-      ru_u32x4* dst = reinterpret_cast<ru_u32x4*>(a.host_rows + (hbase + (int64_t)list_p[k] * ps + o) * a.row_bytes) + c;
-      *dst = *src;
-    }
-    if (a.host_scales)
-      for (int x = tid; x < ncopy * ps; x += kRuThreads) {
-        const int k = x >> lps, o = x & (ps - 1);
-        a.host_scales[hbase + (int64_t)list_p[k] * ps + o] = a.pool_scales[(int64_t)list_g[k] * ps + o];
-      }
+  // the pages to copy, for k_residency_copy
+  for (int k = tid; k < ncopy; k += kRuThreads) {
+    a.list[((size_t)i * kRuMaxList + k) * 2] = list_p[k];
+    a.list[((size_t)i * kRuMaxList + k) * 2 + 1] = list_g[k];
   }
+  if (tid == 0) a.ncopy[i] = ncopy;
 
   // 2. demotion: the d smallest (stamp, page) among the candidates
   int d = 0;
@@ -234,6 +225,40 @@ __global__ __launch_bounds__(kRuThreads) void k_update_residency(RuArgs a, State
   }
 }
 
+// Copy of the listed pages into the host store: request blockIdx.y, the
+// grid's x workgroups stride over its pages 64 bytes per thread, then over
+// its fp8 scales. Writes go over PCIe into the mapped pinned store.
+__global__ __launch_bounds__(256) void k_residency_copy(RuArgs a, StateView v) {
+  const int i = blockIdx.y;
+  const int r = a.req_ids[i];
+  if (r < 0 || r >= v.max_requests) return;
+  const int n = a.ncopy[i];
+  const int ps = v.page_size, lps = v.log2_ps;
+  const int CH = a.row_bytes / 16;
+  const int per_page = ps * CH;
+  const int64_t hbase = v.host_base[r];
+  const int32_t* lst = a.list + (size_t)i * kRuMaxList * 2;
+  const int stride = gridDim.x * 256;
+  // 4 consecutive 16-byte chunks of one page per thread (a page is a
+  // multiple of 4 chunks: 64 B per lane in flight, 4 KiB per wave)
+  for (int x = (blockIdx.x * 256 + threadIdx.x) * 4; x < n * per_page; x += stride * 4) {
+    const int k = x / per_page, rem = x - k * per_page;
+    const int lp = lst[2 * k], gp = lst[2 * k + 1];
+    const ru_u32x4* src = reinterpret_cast<const ru_u32x4*>(a.pool_rows + (int64_t)gp * ps * a.row_bytes) + rem;
+    ru_u32x4* dst = reinterpret_cast<ru_u32x4*>(a.host_rows + (hbase + (int64_t)lp * ps) * a.row_bytes) + rem;
+    const ru_u32x4 t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
+    dst[0] = t0;
+    dst[1] = t1;
+    dst[2] = t2;
+    dst[3] = t3;
+  }
+  if (a.host_scales)
+    for (int x = blockIdx.x * 256 + threadIdx.x; x < n * ps; x += stride) {
+      const int k = x >> lps, o = x & (ps - 1);
+      a.host_scales[hbase + (int64_t)lst[2 * k] * ps + o] = a.pool_scales[(int64_t)lst[2 * k + 1] * ps + o];
+    }
+}
+
 hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_req, const int32_t* budget,
                                   int32_t max_copy, int32_t max_demote, int32_t* freed_out, int32_t* counts_out,
                                   hipStream_t s) {
@@ -249,7 +274,16 @@ hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_
   a.row_bytes = (int)p->sz.row_bytes;
   a.freed_out = freed_out;
   a.counts_out = counts_out;
+  a.list = reinterpret_cast<int32_t*>(p->state + p->off.ru_list);
+  a.ncopy = reinterpret_cast<int32_t*>(p->state + p->off.ru_ncopy);
   k_update_residency<<<n_req, kRuThreads, 0, s>>>(a, make_view(p));
+  if (max_copy > 0) {
+    // enough workgroups to keep many PCIe writes in flight, sized for the
+    // largest copy allowed; surplus workgroups exit at once
+    const int64_t quads = (int64_t)max_copy * p->d.page_size * (p->sz.row_bytes / 16) / 4;
+    const int per_req = (int)std::max<int64_t>(1, std::min<int64_t>((quads + 255) / 256, std::max(1, 2048 / n_req)));
+    k_residency_copy<<<dim3(per_req, n_req), 256, 0, s>>>(a, make_view(p));
+  }
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
 }
