@@ -55,7 +55,7 @@ struct RsScratch {
   int32_t* mdst;                  // [batch][K] pool row a missed position is copied to, else -1
   int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
   int32_t* mold;                  // [batch][K] token that slot held before (or -1)
-  uint32_t* ticket;               // [2] roles handed out, workgroups exited
+  uint32_t* ticket;               // [0]: roles handed out ([1] unused)
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
 
@@ -587,11 +587,18 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
     const int i = q / sc.parts;
     copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts);
   }
-  // the last workgroup of the grid (all have taken their roles) clears the
-  // tickets for the next launch
-  if (tid == 0 && atomicAdd(&sc.ticket[1], 1u) == gridDim.x - 1) {
-    sc.ticket[0] = 0;
-    sc.ticket[1] = 0;
+  // The workgroup with ticket 0 (a bookkeeper, done with its request)
+  // clears the ticket counter for the next launch once every workgroup has
+  // taken its ticket: a bounded wait for workgroups that only need resources
+  // to start, while no other workgroup waits for this one any more.
+  if (role == 0 && tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&sc.ticket[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+      if (++spins > kSpinLimit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, 0u, 0xFFFFFFFEu);
+    __hip_atomic_store(&sc.ticket[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
