@@ -103,6 +103,41 @@ def test_topk_ties_and_sizes(K):
         pool.close()
 
 
+def test_topk_many_requests():
+    """The tie, magnitude and length cases of test_topk_ties_and_sizes
+    repeated over 40 requests in one call (360 filter workgroups, 40 select
+    workgroups), two calls each."""
+    rng = np.random.default_rng(11)
+    K, R, max_ctx = 2048, 40, 70000
+    pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=R, max_context=max_ctx,
+                      kv_dtype="bf16", top_k=K, hot_rows=2 * K, max_batch=R, max_q_rows=16,
+                      host_rows=R * max_ctx)
+    try:
+        lens = [0, 1, K, K + 1, 5000, 2049, 65537, max_ctx] * (R // 8)
+        stride = 70016
+        sc = rng.standard_normal((R, stride)).astype(np.float32)
+        for r in range(0, R, 8):
+            sc[r + 1] = -0.0
+            sc[r + 2] = rng.integers(-2, 3, stride)
+            sc[r + 3] = 1.0
+            sc[r + 5] *= 1e-30
+            sc[r + 6, 100:200] = 1e38
+            sc[r + 7, rng.integers(0, max_ctx, 3000)] = 7.25
+        for r, L in enumerate(lens):
+            pool.set_residency(r, L, r * max_ctx, None)
+        d_sc = torch.from_numpy(sc).cuda()
+        req = torch.arange(R, dtype=torch.int32, device="cuda")
+        idx = torch.full((R, K), -5, dtype=torch.int32, device="cuda")
+        for rep in range(2):
+            pool.select_topk(d_sc, req, idx)
+            got = idx.cpu().numpy()
+            for r, L in enumerate(lens):
+                assert np.array_equal(got[r], select_topk(sc[r], L, K)), f"req {r} L={L} rep {rep}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
 def test_fp8_codes_exhaustive_single_row():
     """With K = 1 the output is the selected row's value part exactly, so
     every finite e4m3 code, widened by the kernel and scaled, must equal the
