@@ -260,6 +260,11 @@ hs_status hs_resolve_rows(hs_pool* pool, const int32_t* idx, const int32_t* req_
  *            over the present rows j (fp8 rows are code * row scale)
  *   lse_out  device fp32 [n_req][q_per_req][n_heads] = log sum_j exp(...), or NULL
  * With no present rows the output is 0 and lse is -inf.
+ * The launch shape (query rows per workgroup, plan tiles per workgroup) is
+ * chosen from the batch size; two environment variables read at the first
+ * call override it for tuning: HS_ATTN_QB (2 or 4 blocks of 16 query rows)
+ * and HS_ATTN_TILES_PER_SPLIT (32-row tiles per workgroup). Results agree
+ * to rounding under any shape.
  * Errors: INVALID_ARGUMENT, CAPACITY (n_req > max_batch or
  * q_per_req * n_heads > max_q_rows), UNSUPPORTED (dtype combination). */
 hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype,
