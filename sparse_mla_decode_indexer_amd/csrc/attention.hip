@@ -257,6 +257,9 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   const int tr_i = (lane & 15) >> 2, tr_c = lane & 3;
   const int v_off0 = krow(kg, tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
   const int v_off1 = krow(kg, 4 + tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
+  // K operand reads (QK): lane (kg, ln) reads chunk 36*half + 4*kk + kg of
+  // tile row 16*rb + ln
+  const int k_off = swz(ln, 36 * half + kg) * 16;
   float m_run = -INFINITY, lpart = 0.f;
 
   // One tile: wait for it, start the gather of tile t + 2 into `nxt` (the
@@ -284,12 +287,14 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       lds_sync();
     }
     // QK partial over key dims 288*half .. +288, all 32 rows of the tile
+    // (operand addresses: one per-lane base plus constant offsets)
     f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    const uint8_t* Tk = T + k_off;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(T + swz(16 * rb + ln, 36 * half + 4 * kk + kg) * 16);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Tk + (16 * rb * kRowChunks + 4 * kk) * 16);
         sacc[rb] = mfma16(a, qop[kk], sacc[rb]);
       }
     }
