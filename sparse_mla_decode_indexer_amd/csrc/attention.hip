@@ -409,8 +409,10 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
 // Thread (row, 4 dims): kBatch partial loads are in flight together; kBatch
 // is the power of two >= the split count (at most 32), so one round trip
-// covers the usual split counts without many padding loads.
-constexpr int kCombineThreads = 256;
+// covers the usual split counts without many padding loads. One-wave
+// workgroups: a single request's 128 query rows (16K threads) then spread
+// over every CU instead of a quarter of them.
+constexpr int kCombineThreads = 64;
 template <int kBatch>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, int QR, int n_splits,
                                                                   const float* __restrict__ part_o,
