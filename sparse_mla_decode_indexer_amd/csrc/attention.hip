@@ -16,7 +16,7 @@
 //     no registers), through a ring of three buffers: tiles t+1 and t+2
 //     are in flight while tile t is computed, and the queries load under
 //     the first gathers; fp8 codes land raw and are widened to bf16 in LDS (exact);
-//     absent rows read a zero row; rows sit 73 chunks of 16 bytes apart in
+//     absent rows read zeros; rows sit 73 chunks of 16 bytes apart in
 //     LDS (one pad chunk), so the MFMA operand reads of 16 rows at one
 //     column hit distinct banks and operand addresses are a base plus an
 //     immediate offset;
@@ -68,6 +68,19 @@ constexpr int kRawTileBytes = kTile * kRawChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.f;  // see the online softmax in k_attn_mfma
+// Tile gathers. When the pool spans at most kBufMaxBytes, rows are read
+// through a raw buffer view of the pool (buffer_load ... lds, 32-bit
+// offsets): absent rows and pad chunks take an offset past the view's end
+// and read zeros. Larger pools use global_load_lds with 64-bit addresses and
+// a zero row. The buffer form also keeps the compiler's LDS waits exact:
+// with a global_load_lds in flight it treats the LDS counter as unordered
+// and waits for every LDS read to finish before using any of them.
+constexpr uint64_t kBufMaxBytes = 0xFFFF0000ull;
+constexpr uint32_t kBufOob = 0xFFFF0000u;  // offset past any buffer view
+constexpr int kBufWord3 = 0x00020000;      // descriptor word 3: 32-bit data format
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kPvAhead = 3;  // V^T operand blocks loaded ahead of their MFMAs
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -141,11 +154,11 @@ __device__ inline float sum_across_kg(float x) {
 // LDS chunk position of 16-byte chunk c of tile row r.
 __device__ inline int swz(int r, int c) { return r * kRowChunks + c; }
 
-template <bool FP8, int QB>
+template <bool FP8, int QB, bool BUF>
 __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     const uint16_t* __restrict__ q, int QR, const int32_t* __restrict__ plan, int K,
     const uint8_t* __restrict__ pool, const float* __restrict__ pool_scales, int64_t pool_rows_n,
-    const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
+    uint32_t pool_bytes, const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
     float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o,
     float* __restrict__ part_lse, uint32_t* __restrict__ err) {
   // A ring of three distinct LDS buffers (not one indexed array) so that
@@ -233,13 +246,21 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 #pragma unroll
     for (int k = 0; k < kIssue; ++k) rr[k] = t < nt ? prow_s[t * kTile + rowk[k]] : -1;
   };
+  const __amdgpu_buffer_rsrc_t pool_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)pool, 0, (int)pool_bytes, kBufWord3);
   auto issue = [&](const int* rr, uint8_t* dst) {
 #pragma unroll
     for (int k = 0; k < kIssue; ++k) {
-      constexpr size_t rb = FP8 ? kRowDim : 2 * kRowDim;
+      constexpr int rb = FP8 ? kRowDim : 2 * kRowDim;
       const bool real = (rr[k] | coff[k]) >= 0;
-      const uint8_t* src = real ? pool + (size_t)rr[k] * rb + coff[k] : zero_row;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + (k * kAttThreads + wave_s * 64) * 16), 16, 0, 0);
+      lds_void_t* ld = (lds_void_t*)(dst + (k * kAttThreads + wave_s * 64) * 16);
+      if constexpr (BUF) {
+        const uint32_t off = real ? (uint32_t)rr[k] * rb + (uint32_t)coff[k] : kBufOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_rs, ld, 16, off, 0, 0, 0);
+      } else {
+        const uint8_t* src = real ? pool + (size_t)rr[k] * rb + coff[k] : zero_row;
+        __builtin_amdgcn_global_load_lds(src, ld, 16, 0, 0);
+      }
     }
   };
   constexpr int kWaitOne = vmcnt_imm(kIssue);      // all but the last tile issued
@@ -347,13 +368,25 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 #pragma unroll
       for (int b = 0; b < 16; ++b) acc[b] *= alpha;
     }
+    u32x4_t va[16];
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       const u32x2_t x = tr_load(T + v_off0 + 32 * b);
       const u32x2_t y = tr_load(T + v_off1 + 32 * b);
-      const u32x4_t A = u32x4_t{x[0], x[1], y[0], y[1]};
-      acc[b] = mfma16(A, bhi, acc[b]);
-      acc[b] = mfma16(A, blo, acc[b]);
+      va[b] = u32x4_t{x[0], x[1], y[0], y[1]};
+    }
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      acc[b] = mfma16(va[b], bhi, acc[b]);
+      acc[b] = mfma16(va[b], blo, acc[b]);
+    }
+    // Instruction order: the operand loads run kPvAhead blocks ahead of
+    // their MFMAs, so LDS latency overlaps the MFMAs of earlier blocks.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if (b + kPvAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   };
 
@@ -581,17 +614,27 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const bool fp8 = p->d.kv_dtype != HS_BF16;
   const float* sc = fp8 ? p->pool_scales : nullptr;
-#define HS_ATTN_LAUNCH(F, B)                                                                                  \
-  k_attn_mfma<F, B><<<grid, 128 * (B), 0, s>>>(q16, QR, plan, K, p->pool_rows, sc, p->pool_rows_n, zero_row, c2, \
-                                               tps, splits, out, lse_out, part_o, part_lse, err)
-  if (fp8 && qb == 4)
-    HS_ATTN_LAUNCH(true, 4);
-  else if (fp8)
-    HS_ATTN_LAUNCH(true, 2);
-  else if (qb == 4)
-    HS_ATTN_LAUNCH(false, 4);
-  else
-    HS_ATTN_LAUNCH(false, 2);
+  const uint64_t pool_bytes = (uint64_t)p->pool_rows_n * (fp8 ? kRowDim : 2 * kRowDim);
+  const bool buf = pool_bytes <= kBufMaxBytes;
+  const uint32_t pb32 = buf ? (uint32_t)pool_bytes : 0u;
+#define HS_ATTN_LAUNCH(F, B, U)                                                                           \
+  k_attn_mfma<F, B, U><<<grid, 128 * (B), 0, s>>>(q16, QR, plan, K, p->pool_rows, sc, p->pool_rows_n, pb32, \
+                                                  zero_row, c2, tps, splits, out, lse_out, part_o, part_lse, err)
+#define HS_ATTN_LAUNCH_QB(F, U) \
+  if (qb == 4)                  \
+    HS_ATTN_LAUNCH(F, 4, U);    \
+  else                          \
+    HS_ATTN_LAUNCH(F, 2, U)
+  if (fp8 && buf) {
+    HS_ATTN_LAUNCH_QB(true, true);
+  } else if (fp8) {
+    HS_ATTN_LAUNCH_QB(true, false);
+  } else if (buf) {
+    HS_ATTN_LAUNCH_QB(false, true);
+  } else {
+    HS_ATTN_LAUNCH_QB(false, false);
+  }
+#undef HS_ATTN_LAUNCH_QB
 #undef HS_ATTN_LAUNCH
   if (splits > 1) {
     const int rows = n_req * QR;

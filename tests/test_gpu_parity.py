@@ -377,6 +377,111 @@ def test_attention_score_jumps(kv, shape):
         pool.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attention_absent_rows_over_nan_lds(kv):
+    """Absent plan entries read zeros, whatever the tile buffers held
+    before: a first call gathers NaN rows into every tile buffer, then a
+    plan with absent entries (a ragged tail and scattered -1s) over finite
+    rows must give finite outputs within the fp64 bar. A gather that left
+    stale bytes in place of an absent row would turn its zero weight into
+    NaN."""
+    from oracle import bf16_decode, e4m3fn_decode
+    from gpu_helpers import ATTN_TOL, attn_rel_err
+    rng = np.random.default_rng(11)
+    K, H, n_rows = 2048, 128, 4096
+    pool = TieredPool(page_size=64, num_pool_pages=n_rows // 64, max_requests=1, max_context=n_rows,
+                      kv_dtype=kv, top_k=K, hot_rows=4096, max_batch=1, max_q_rows=H, host_rows=64)
+    try:
+        sm = 1.0 / np.sqrt(W.ROW_DIM)
+        q = rng.standard_normal((H, W.ROW_DIM)).astype(np.float32)
+        qb = W.f32_to_bf16_bits(q)
+        d_q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16).reshape(1, 1, H, W.ROW_DIM)
+        out = torch.empty((1, 1, H, W.NOPE_DIM), device="cuda")
+        # 1. every row NaN (bf16 0x7FC0; e4m3fn 0x7F), every plan entry present
+        if kv == "bf16":
+            pool.pool_row_view().view(torch.int16).fill_(0x7FC0)
+        else:
+            pool.pool_row_view().fill_(0x7F)
+            pool.pool_scales.fill_(1.0)
+        full = torch.from_numpy(rng.permutation(n_rows)[:K].astype(np.int32)).cuda().reshape(1, K)
+        pool.sparse_mla_decode(d_q, full, sm, out, None)
+        torch.cuda.synchronize()
+        # 2. finite rows, absent entries
+        x = rng.standard_normal((n_rows, W.ROW_DIM)).astype(np.float32)
+        if kv == "bf16":
+            bits = W.f32_to_bf16_bits(x)
+            pool.pool_row_view().copy_(torch.from_numpy(bits.view(np.uint8).reshape(n_rows, -1)).cuda())
+            logical = bf16_decode(bits)
+        else:
+            codes, sc = W.f32_rows_to_fp8(x)
+            pool.pool_row_view().copy_(torch.from_numpy(codes).cuda())
+            pool.pool_scales.copy_(torch.from_numpy(sc).cuda())
+            logical = e4m3fn_decode(codes) * sc[:, None].astype(np.float64)
+        plan = rng.permutation(n_rows)[:K].astype(np.int32)
+        plan[rng.integers(0, K, 300)] = -1
+        plan[-100:] = -1
+        live = plan >= 0
+        d_plan = torch.from_numpy(plan).cuda().reshape(1, K)
+        pool.sparse_mla_decode(d_q, d_plan, sm, out, None)
+        o = out.cpu().numpy().reshape(H, -1)
+        assert np.isfinite(o).all()
+        o_ref, _ = mla_attention(bf16_decode(qb), logical[plan[live]], sm)
+        e = attn_rel_err(o, o_ref)
+        assert e <= ATTN_TOL, f"{kv}: attention rel err {e:.3e}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attention_pool_over_4gib(kv):
+    """A pool of more than 4 GiB of rows (65,536 bf16 or 131,072 fp8 pages of
+    64 rows): the gathers then use 64-bit addresses instead of a 32-bit
+    buffer view. The plan's rows are spread over the whole pool, the highest
+    ones past the 4 GiB mark, with absent entries; every head within the
+    fp64 bar."""
+    from oracle import bf16_decode, e4m3fn_decode
+    from gpu_helpers import ATTN_TOL, attn_rel_err
+    rng = np.random.default_rng(12)
+    K, H = 2048, 128
+    pages = 65536 if kv == "bf16" else 131072
+    n_rows = pages * 64
+    pool = TieredPool(page_size=64, num_pool_pages=pages, max_requests=1, max_context=1 << 16,
+                      kv_dtype=kv, top_k=K, hot_rows=4096, max_batch=1, max_q_rows=H, host_rows=64)
+    try:
+        assert n_rows * pool.row_bytes > (1 << 32)
+        top = n_rows - 16 + np.arange(16)        # the pool's last 16 rows
+        plan = np.concatenate([np.sort(rng.choice(n_rows - 16, K - 16, replace=False)), top]).astype(np.int32)
+        assert int(plan.max()) * pool.row_bytes >= (1 << 32)
+        x = rng.standard_normal((K, W.ROW_DIM)).astype(np.float32)
+        d_idx = torch.from_numpy(plan.astype(np.int64)).cuda()
+        if kv == "bf16":
+            bits = W.f32_to_bf16_bits(x)
+            pool.pool_row_view()[d_idx] = torch.from_numpy(bits.view(np.uint8).reshape(K, -1)).cuda()
+            logical = bf16_decode(bits)
+        else:
+            codes, sc = W.f32_rows_to_fp8(x)
+            pool.pool_row_view()[d_idx] = torch.from_numpy(codes).cuda()
+            pool.pool_scales[d_idx] = torch.from_numpy(sc).cuda()
+            logical = e4m3fn_decode(codes) * sc[:, None].astype(np.float64)
+        live = np.ones(K, bool)
+        live[rng.integers(0, K, 50)] = False
+        q = rng.standard_normal((H, W.ROW_DIM)).astype(np.float32)
+        qb = W.f32_to_bf16_bits(q)
+        d_q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16).reshape(1, 1, H, W.ROW_DIM)
+        d_plan = torch.from_numpy(np.where(live, plan, -1).astype(np.int32)).cuda().reshape(1, K)
+        out = torch.empty((1, 1, H, W.NOPE_DIM), device="cuda")
+        sm = 1.0 / np.sqrt(W.ROW_DIM)
+        pool.sparse_mla_decode(d_q, d_plan, sm, out, None)
+        o = out.cpu().numpy().reshape(H, -1)
+        o_ref, _ = mla_attention(bf16_decode(qb), logical[live], sm)
+        e = attn_rel_err(o, o_ref)
+        assert e <= ATTN_TOL, f"{kv}: attention rel err {e:.3e}"
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
 def test_imported_prefix_start_shared_host_rows():
     """None-resident start from an imported prefix ([P2] residency state 3,
     and P/D imports landing host-side): request 1 reuses request 0's prefix,
