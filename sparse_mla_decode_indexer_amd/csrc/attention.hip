@@ -81,6 +81,7 @@ constexpr int kBufWord3 = 0x00020000;      // descriptor word 3: 32-bit data for
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 constexpr int kPvAhead = 3;  // V^T operand blocks loaded ahead of their MFMAs
+constexpr int kQkAhead = 3;  // K operand steps loaded ahead of their MFMAs
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -311,13 +312,21 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     // (operand addresses: one per-lane base plus constant offsets)
     f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     const uint8_t* Tk = T + k_off;
+    u32x4_t ka[kKSteps][2];
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) ka[kk][rb] = *reinterpret_cast<const u32x4_t*>(Tk + (16 * rb * kRowChunks + 4 * kk) * 16);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma16(ka[kk][rb], qop[kk], sacc[rb]);
+    // loads kQkAhead key steps ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kQkAhead, 0);
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Tk + (16 * rb * kRowChunks + 4 * kk) * 16);
-        sacc[rb] = mfma16(a, qop[kk], sacc[rb]);
-      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if (kk + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     sbuf[half][qb][0][lane] = sacc[0];
     sbuf[half][qb][1][lane] = sacc[1];
