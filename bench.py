@@ -2,6 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload single-128k]
 
+Growing-context workloads (agent16, agent16-b) are timed with every
+request at its first step's context length.
+
 A step is the whole hot path for every request of the workload: top-K over
 the indexer scores -> fused resolve (resident / hot / miss copy over PCIe)
 -> sparse MLA attention over the K resolved rows. Inputs (scores and
@@ -14,7 +17,9 @@ pool state, with HIP events (on the stream the kernels run on) around each
 of the three entry points (a spin kernel first lets the host queue run
 ahead, so the events see GPU time only). The entry point with the largest
 average duration is reported against its bound (PCIe for the miss copy,
-HBM for the scans and gathers) with its algorithmic bytes per launch;
+HBM for the scans and gathers, MFMA for attention when its FLOP per
+algorithmic byte is above the bf16 ridge, as with fp8 rows or four query
+tokens per request) with its algorithmic bytes (or FLOPs) per launch;
 `traffic` is the HBM bytes per launch its kernels actually moved, from the
 committed counter summary profiles/decode_step_<workload>_hbm_traffic.json
 (null when absent or taken on other kernel sources).
@@ -88,10 +93,11 @@ def main():
     wl = W.generate(spec)
     if spec.growth is not None and T > spec.steps:
         raise SystemExit(f"{spec.name} defines {spec.steps} steps")
-    sched = W.context_schedule(spec, wl.ctx0, T) if spec.growth is not None else \
-        np.broadcast_to(wl.ctx0, (T, spec.n_req))
-    if spec.growth is not None:
-        raise SystemExit("growing-context workloads are parity cases, not bench lines")
+    # Growing (agent) workloads are timed at their first step's context: the
+    # growth between steps is the engine writing new rows, outside the step,
+    # so every timed step sees the turn-1 length (the parity tests follow
+    # the full growing schedule).
+    sched = np.broadcast_to(wl.ctx0, (T, spec.n_req))
     dev = "cuda"
     torch.cuda.set_device(0)
     pool = Hn.make_pool(wl, device=dev)
@@ -192,22 +198,32 @@ def main():
         dur = np.array([[ev[a].elapsed_time(ev[a + 1]) for a in range(3)] for ev in evs])  # ms
         avg = dur.mean(axis=0) * 1e3  # us
         names = ["select_topk", "resolve_rows", "sparse_mla_decode"]
+        # attention is a bf16 MFMA contraction (fp8 rows are widened to
+        # bf16): priced against MFMA when its FLOP per algorithmic byte is
+        # above the ridge, else against HBM
+        attn_mfma = flops_attn / b_attn > MFMA_BF16_PEAK_TFS * 1e3 / HBM_PEAK_GBS
         per = {
-            "select_topk": dict(bound="hbm", bytes=b_topk, peak=HBM_PEAK_GBS),
-            "resolve_rows": dict(bound="pcie", bytes=b_pcie, peak=PCIE_PEAK_GBS),
-            "sparse_mla_decode": dict(bound="hbm", bytes=b_attn, peak=HBM_PEAK_GBS),
+            "select_topk": dict(bound="hbm", bytes=b_topk, peak=HBM_PEAK_GBS, unit="GB/s"),
+            "resolve_rows": dict(bound="pcie", bytes=b_pcie, peak=PCIE_PEAK_GBS, unit="GB/s"),
+            "sparse_mla_decode": dict(bound="mfma", flops=flops_attn, peak=MFMA_BF16_PEAK_TFS,
+                                      unit="TFLOP/s", bytes=b_attn) if attn_mfma else
+                                 dict(bound="hbm", bytes=b_attn, peak=HBM_PEAK_GBS, unit="GB/s"),
         }
         dom = int(np.argmax(avg))
         name = names[dom]
         d = per[name]
-        achieved = d["bytes"] / (avg[dom] * 1e-6) / 1e9
+        if d["bound"] == "mfma":
+            achieved = d["flops"] / (avg[dom] * 1e-6) / 1e12
+        else:
+            achieved = d["bytes"] / (avg[dom] * 1e-6) / 1e9
         roof = {"kernel": name, "kernels": ENTRY_KERNELS[name], "bound": d["bound"],
-                "achieved": round(achieved, 2), "peak": d["peak"], "unit": "GB/s",
+                "achieved": round(achieved, 2), "peak": d["peak"], "unit": d["unit"],
                 "frac": round(achieved / d["peak"], 4),
                 "traffic": measured_traffic(spec.name, ENTRY_KERNELS[name]),
                 "avg_us": {n: round(float(a), 2) for n, a in zip(names, avg)},
                 "bytes_per_launch": {n: int(per[n]["bytes"]) for n in names},
-                "attention_tflops": round(flops_attn / (avg[2] * 1e-6) / 1e12, 2)}
+                "attention_tflops": round(flops_attn / (avg[2] * 1e-6) / 1e12, 2),
+                "attention_mfma_frac": round(flops_attn / (avg[2] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
 
     # hit-only replay: the last step's inputs again, after that step filled the
     # hot buffers, so every selected row is resident or hot (no PCIe)
@@ -250,6 +266,8 @@ def main():
         "config": {"workload": spec.name, "requests": R, "context": int(lens.max()),
                    "kv_dtype": spec.kv_dtype, "heads": spec.heads, "q_per_req": spec.q_per_req,
                    "top_k": Kt, "hot_rows": S, "residency": spec.residency,
+                   **({"growth": "context frozen at the first step's length"}
+                      if spec.growth is not None else {}),
                    **({"layers": spec.layers} if spec.layers > 1 else {})},
         **({"layer_steps_per_s": round(value * spec.layers, 1)} if spec.layers > 1 else {}),
         "rows_resolved_per_s": round(rows_per_step * value, 1),
