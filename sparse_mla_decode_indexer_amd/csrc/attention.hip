@@ -179,7 +179,11 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   constexpr int kAttThreads = 128 * QB;
   constexpr int kQPerWG = 16 * QB;
 
-  const int sp = blockIdx.x, hg = blockIdx.y, i = blockIdx.z;
+  // Grid (splits, requests, query-row groups): the hardware deals
+  // consecutive workgroups round-robin to the 8 XCDs, so when splits x
+  // requests is a multiple of 8 the query-row groups of one (request,
+  // split), which gather the same rows, all run on one XCD and share its L2.
+  const int sp = blockIdx.x, i = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, ln = lane & 15;
   const int qb = wave % QB, half = wave / QB;  // query block; key-dim half (QK) and value-dim half (PV)
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
 // Thread (row, 4 dims): kBatch partial loads are in flight together; kBatch
-// is the power of two >= the split count (at most 32), so one round trip
+// is the power of two >= the split count (2 to 32), so one round trip
 // covers the usual split counts without many padding loads. One-wave
 // workgroups: a single request's 128 query rows (16K threads) then spread
 // over every CU instead of a quarter of them.
@@ -619,7 +623,7 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   float* part_o = reinterpret_cast<float*>(p->state + p->off.at_part_o);
   float* part_lse = reinterpret_cast<float*>(p->state + p->off.at_part_lse);
   const float c2 = sm_scale * kLog2e;
-  const dim3 grid(splits, n_hg, n_req);
+  const dim3 grid(splits, n_req, n_hg);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const bool fp8 = p->d.kv_dtype != HS_BF16;
   const float* sc = fp8 ? p->pool_scales : nullptr;
@@ -650,7 +654,9 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
     const int64_t threads = (int64_t)rows * (kNope / 4);
     const int nb = (int)((threads + kCombineThreads - 1) / kCombineThreads);
 #define HS_COMBINE(B) k_attn_combine<B><<<nb, kCombineThreads, 0, s>>>(rows, QR, splits, part_o, part_lse, out, lse_out)
-    if (splits <= 4)
+    if (splits <= 2)
+      HS_COMBINE(2);
+    else if (splits <= 4)
       HS_COMBINE(4);
     else if (splits <= 8)
       HS_COMBINE(8);
