@@ -31,4 +31,5 @@ from .hisparse_oracle import (  # noqa: F401
     resolve_step,
     select_topk,
 )
+from .indexer import indexer_scores  # noqa: F401
 from .residency import PageState, update_residency  # noqa: F401

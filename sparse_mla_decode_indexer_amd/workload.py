@@ -388,3 +388,38 @@ class QueryStream:
         if s.q_dtype == "bf16":
             return f32_to_bf16_bits(q)
         return q
+
+
+# ---------------------------------------------------------------- indexer inputs
+INDEXER_DIM = 128
+INDEXER_HEADS = 64
+
+
+class IndexerInputs:
+    """Synthetic inputs of the indexer score step (no method arithmetic).
+
+    Per request slot r: indexer keys [capacity, 128] as bf16 bits, drawn
+    N(0, 1) per element from the request's own stream. Per step: indexer
+    queries [R, H, 128] (bf16 bits, N(0, 1)) and head weights [R, H] (fp32,
+    N(0, 1) / sqrt(H)). Seeded from the workload's master seed with a stream
+    of its own, so the latent-row and score streams are unchanged.
+    """
+
+    def __init__(self, seed: int, n_req: int, capacity: np.ndarray, heads: int = INDEXER_HEADS):
+        ss = np.random.SeedSequence([seed, 7]).spawn(2)
+        self.heads = heads
+        self.n_req = n_req
+        self.capacity = np.asarray(capacity, dtype=np.int64)
+        self.keys = []
+        for r, rs in enumerate(ss[0].spawn(n_req)):
+            g = np.random.Generator(np.random.PCG64(rs))
+            k = g.standard_normal((int(self.capacity[r]), INDEXER_DIM), dtype=np.float32)
+            self.keys.append(f32_to_bf16_bits(k))
+        self.g = np.random.Generator(np.random.PCG64(ss[1]))
+
+    def next(self) -> Tuple[np.ndarray, np.ndarray]:
+        """(queries as bf16 bits [R, H, 128], weights fp32 [R, H]) of the next step."""
+        q = self.g.standard_normal((self.n_req, self.heads, INDEXER_DIM), dtype=np.float32)
+        w = (self.g.standard_normal((self.n_req, self.heads), dtype=np.float32)
+             / np.float32(math.sqrt(self.heads))).astype(np.float32)
+        return f32_to_bf16_bits(q), w
