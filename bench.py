@@ -243,6 +243,7 @@ def main():
         cold["resolve_pcie_frac"] = round(cold["resolve_pcie_gbs"] / PCIE_PEAK_GBS, 4)
 
     resid = None if args.no_roofline else residency_probe(pool, buf, spec)
+    indexer = None if args.no_roofline else indexer_probe(pool, buf, spec, wl)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -281,6 +282,7 @@ def main():
         "cold_step": cold,
         "hit_only_replay": hit,
         "residency_manager": resid,
+        "indexer": indexer,
     }
     pool.close()
     print(json.dumps(line))
@@ -397,6 +399,46 @@ def residency_probe(pool, buf, spec, pages_per_call: int = 64, calls: int = 4):
             "copy_call_us": round(copy_ms * 1e3 / calls, 2), "copy_gbs": round(gbs, 2),
             "pcie_peak_gbs": PCIE_PEAK_GBS, "copy_frac": round(gbs / PCIE_PEAK_GBS, 4),
             "release_call_us": round(rel_ms * 1e3, 2), "released_pages": released}
+
+
+def indexer_probe(pool, buf, spec, wl, heads: int = 64, calls: int = 20):
+    """Indexer scores (upstream of the step, which starts from scores) for
+    every request of the workload at its context length: 64 heads, bf16
+    queries and 128-dim bf16 indexer keys drawn on the device from a seeded
+    generator, fp32 head weights. HIP events around `calls` back-to-back
+    launches on the stream the kernel runs on (a spin kernel first lets the
+    host queue run ahead); priced against HBM by the bytes the formula must
+    read and write (keys 256 B per token, queries and weights, fp32 scores)."""
+    import torch
+    R = spec.n_req
+    dev = buf.req_ids.device
+    g = torch.Generator(device=dev).manual_seed(spec.seed)
+    maxc = int(wl.max_context)
+    ik = torch.empty((R, maxc, 128), dtype=torch.bfloat16, device=dev)
+    for r in range(R):  # one request at a time (bounded fp32 temporary)
+        ik[r] = torch.randn((maxc, 128), generator=g, device=dev).to(torch.bfloat16)
+    iq = torch.randn((R, heads, 128), generator=g, device=dev).to(torch.bfloat16)
+    iw = torch.randn((R, heads), generator=g, device=dev) / heads ** 0.5
+    out = torch.empty((R, buf.scores.shape[-1]), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        pool.indexer_scores(iq, iw, ik, buf.req_ids, out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2e8))
+    e0.record(stream)
+    for _ in range(calls):
+        pool.indexer_scores(iq, iw, ik, buf.req_ids, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    tokens = int(np.asarray(wl.ctx0, dtype=np.int64).sum())
+    nbytes = tokens * (128 * 2 + 4) + R * heads * (128 * 2 + 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del ik
+    return {"calls": calls, "heads": heads, "tokens_per_call": tokens, "avg_us": round(us, 2),
+            "bytes_per_call": nbytes, "gbs": round(gbs, 1), "hbm_peak_gbs": HBM_PEAK_GBS,
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, host_scores, host_q, sched, budget_s):

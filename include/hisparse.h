@@ -3,6 +3,7 @@
  *
  * One decode step of one sparse-MLA layer over a latent KV cache whose pages
  * live either in GPU memory or only in pinned host memory:
+ *   hs_indexer_scores   per-token indexer scores (upstream of the step);
  *   hs_select_topk      the indexer's top-K over per-token scores;
  *   hs_resolve_rows     one fused pass that turns each selected token into a
  *                       physical pool row: read in place when its page is on
@@ -224,6 +225,30 @@ hs_status hs_set_residency(hs_pool* pool, int32_t req, int32_t context_len,
 hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_stride,
                          const int32_t* req_ids, int32_t n_req, int32_t* idx_out,
                          hipStream_t stream);
+
+/* Indexer scores, the input of hs_select_topk ([P3] §"稀疏MLA的核心思想": the
+ * indexer picks the tokens that enter attention; [P2] §"与 vLLM 栈的集成",
+ * indexer KV item: the indexer keeps a per-token key cache of its own). The
+ * pages give no formula; the one computed (the lightning-indexer form) is,
+ * for each i < n_req, r = req_ids[i] (device int32) and t < L_r (read on the
+ * device):
+ *     scores[i * score_stride + t] = sum_j iw[i][j] * max(0, <iq[i][j], ik_r[t]>)
+ * over heads j < n_heads, in fp32 (exact bf16 products, fp32 sums).
+ *   iq      device bf16 [n_req][n_heads][128], 16-byte aligned
+ *   iw      device fp32 [n_req][n_heads]
+ *   ik      device bf16, 16-byte aligned: token t of request slot r at
+ *           ik + (r * ik_stride + t) * 128 (elements); ik_stride >= max_context
+ *           rows; rows of tokens < L_r must be valid
+ *   n_heads 16, 32, 48 or 64
+ *   scores  device fp32, row i at scores + i * score_stride (score_stride >=
+ *           max_context); entries t >= L_r are left untouched
+ * Graph-capturable like the per-step calls. Errors: INVALID_ARGUMENT,
+ * CAPACITY (n_req > max_batch); a req_ids entry outside [0, max_requests)
+ * raises HS_DEV_REQUEST_RANGE and that row is not written. */
+hs_status hs_indexer_scores(hs_pool* pool, const void* iq, const float* iw, const void* ik,
+                            int64_t ik_stride, int32_t n_heads, const int32_t* req_ids,
+                            int32_t n_req, float* scores, int64_t score_stride,
+                            hipStream_t stream);
 
 /* Fused resolve ([P2] §"混合 HiSparse 的技术实现", state 2: one fused kernel
  * handles the top-K results — resident rows read in place, hot rows read and

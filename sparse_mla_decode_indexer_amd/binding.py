@@ -62,6 +62,7 @@ _SIGS = {
     "hs_host_rows": [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP)],
     "hs_set_residency": [_VP, _I32, _I32, _I64, _I32, _I32, _VP, _VP, _U32, _VP],
     "hs_select_topk": [_VP, _VP, _I64, _VP, _I32, _VP, _VP],
+    "hs_indexer_scores": [_VP, _VP, _VP, _VP, _I64, _I32, _VP, _I32, _VP, _I64, _VP],
     "hs_resolve_rows": [_VP, _VP, _VP, _I32, _VP, _VP, _VP],
     "hs_update_residency": [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _VP],
     "hs_sparse_mla_decode": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
@@ -141,6 +142,12 @@ def select_topk(pool: int, scores: int, score_stride: int, req_ids: int, n_req: 
                 stream: int):
     _check(lib().hs_select_topk(pool, scores, score_stride, req_ids, n_req, idx_out, stream or None),
            "hs_select_topk")
+
+
+def indexer_scores(pool: int, iq: int, iw: int, ik: int, ik_stride: int, n_heads: int, req_ids: int,
+                   n_req: int, scores: int, score_stride: int, stream: int):
+    _check(lib().hs_indexer_scores(pool, iq, iw, ik, ik_stride, n_heads, req_ids, n_req, scores, score_stride,
+                                   stream or None), "hs_indexer_scores")
 
 
 def resolve_rows(pool: int, idx: int, req_ids: int, n_req: int, plan_out: int, counts_out: int,

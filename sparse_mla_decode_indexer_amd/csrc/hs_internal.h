@@ -98,6 +98,9 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
 hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_req,
                                   const int32_t* budget, int32_t max_copy, int32_t max_demote,
                                   int32_t* freed_out, int32_t* counts_out, hipStream_t s);
+hs_status launch_indexer_scores(hs_pool* p, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
+                                int32_t n_heads, const int32_t* req_ids, int32_t n_req, float* scores,
+                                int64_t score_stride, hipStream_t s);
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
                            int32_t q_per_req, int32_t n_heads, const int32_t* plan,
                            float sm_scale, float* out, float* lse_out, hipStream_t s);

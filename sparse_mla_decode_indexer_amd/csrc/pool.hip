@@ -351,6 +351,19 @@ hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_strid
   return launch_topk(pool, scores, score_stride, req_ids, n_req, idx_out, stream);
 }
 
+hs_status hs_indexer_scores(hs_pool* pool, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
+                            int32_t n_heads, const int32_t* req_ids, int32_t n_req, float* scores,
+                            int64_t score_stride, hipStream_t stream) {
+  if (!pool || !iq || !iw || !ik || !req_ids || !scores) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req < 0 || n_heads < 16 || n_heads > 64 || (n_heads % 16)) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch) return HS_ERR_CAPACITY;
+  if (ik_stride < pool->d.max_context || score_stride < pool->d.max_context) return HS_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(iq) | reinterpret_cast<uintptr_t>(ik)) & 15) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req == 0) return HS_OK;
+  return hs::launch_indexer_scores(pool, iq, iw, ik, ik_stride, n_heads, req_ids, n_req, scores, score_stride,
+                                   stream);
+}
+
 hs_status hs_resolve_rows(hs_pool* pool, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
                           int32_t* plan_out, int32_t* counts_out, hipStream_t stream) {
   if (!pool || !idx || !req_ids || !plan_out) return HS_ERR_INVALID_ARGUMENT;

@@ -106,6 +106,14 @@ class TieredPool:
         B.select_topk(self.handle, scores.data_ptr(), scores.stride(0), req_ids.data_ptr(),
                       int(req_ids.numel()), idx_out.data_ptr(), _stream())
 
+    def indexer_scores(self, iq: torch.Tensor, iw: torch.Tensor, ik: torch.Tensor, req_ids: torch.Tensor,
+                       scores: torch.Tensor):
+        """iq bf16 [n, H, 128], iw fp32 [n, H], ik bf16 [max_requests, stride, 128] (request slot r's
+        indexer keys in ik[r]), scores fp32 [n, stride'] (row i gets tokens 0..L_r-1)."""
+        n, H, _ = iq.shape
+        B.indexer_scores(self.handle, iq.data_ptr(), iw.data_ptr(), ik.data_ptr(), ik.stride(0) // ik.stride(1),
+                         H, req_ids.data_ptr(), n, scores.data_ptr(), scores.stride(0), _stream())
+
     def resolve_rows(self, idx: torch.Tensor, req_ids: torch.Tensor, plan_out: torch.Tensor,
                      counts_out: Optional[torch.Tensor] = None):
         B.resolve_rows(self.handle, idx.data_ptr(), req_ids.data_ptr(), int(req_ids.numel()),

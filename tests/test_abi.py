@@ -17,7 +17,7 @@ def _lib():
 def test_exports_every_declared_function():
     L = _lib()
     names = B.header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert set(B._SIGS) == set(names)
@@ -67,5 +67,6 @@ def test_null_handles_rejected_without_device_work():
     assert L.hs_sparse_mla_decode(None, None, 1, 1, 1, 1, None, 0.1, None, None, None) == 1
     assert L.hs_set_residency(None, 0, 0, 0, 0, 0, None, None, 0, None) == 1
     assert L.hs_update_residency(None, None, 1, None, 0, 0, None, None, None) == 1
+    assert L.hs_indexer_scores(None, None, None, None, 0, 64, None, 1, None, 0, None) == 1
     assert L.hs_destroy_pool(None) == 0
     assert B.status_string(2) == "exceeds pool capacity"
