@@ -12,8 +12,8 @@
 // k_indexer_scores: a workgroup of 4 waves takes 256 tokens per pass of one
 // request. Per 16 tokens a wave computes the 16 x H dot products with
 // 16x16x32 bf16 MFMAs (the keys as the A operand straight from global memory,
-// 16 bytes per lane and k-step; the queries as the B operand, loaded once
-// per wave and kept in registers), applies max(0, .) and the head weights in
+// 16 bytes per lane and k-step; the queries as the B operand, read once per
+// workgroup into LDS and kept in registers by each wave), applies max(0, .) and the head weights in
 // fp32 and sums over heads within the lane (head blocks) and across the 16
 // lanes that hold one token's heads. Bound by HBM: 256 bytes of keys per
 // token against 4 bytes of score.
@@ -59,19 +59,24 @@ __global__ __launch_bounds__(kIxThreads) void k_indexer_scores(const uint16_t* _
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane >> 4, ln = lane & 15;
 
-  // B operand of head block hb and k-step kk: head 16hb + ln, dims
-  // 32kk + 8kg .. +8; the lane's head weights
-  ix_u32x4_t qop[HB][4];
-  float wv[HB];
+  // The request's queries (16 * HB heads x 128 dims, bf16) are read once per
+  // workgroup into LDS, then each wave takes its B operands from there: head
+  // block hb, k-step kk: head 16hb + ln, dims 32kk + 8kg .. +8.
+  constexpr int kQChunks = 16 * HB * kIxDim / 8;  // 16-byte chunks
+  __shared__ ix_u32x4_t q_s[kQChunks];
   {
-    const uint16_t* qr = iq + (size_t)i * (16 * HB) * kIxDim;
+    const ix_u32x4_t* qr = reinterpret_cast<const ix_u32x4_t*>(iq + (size_t)i * (16 * HB) * kIxDim);
+    for (int c = threadIdx.x; c < kQChunks; c += kIxThreads) q_s[c] = qr[c];
+  }
+  float wv[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) wv[hb] = iw[(size_t)i * 16 * HB + 16 * hb + ln];
+  __syncthreads();
+  ix_u32x4_t qop[HB][4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qop[hb][kk] = *reinterpret_cast<const ix_u32x4_t*>(qr + (size_t)(16 * hb + ln) * kIxDim + 32 * kk + 8 * kg);
-      wv[hb] = iw[(size_t)i * 16 * HB + 16 * hb + ln];
-    }
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qop[hb][kk] = q_s[((16 * hb + ln) * kIxDim + 32 * kk + 8 * kg) / 8];
   }
   const uint16_t* kr = ik + (size_t)rq * ik_stride * kIxDim;
   float* out = scores + (size_t)i * score_stride;
