@@ -296,12 +296,17 @@ ENTRY_KERNELS = {
 }
 
 
+# Sources the decode-step kernels (top-K, resolve, attention) are built from:
+# the counters recorded for them stay valid while these files are unchanged.
+STEP_SOURCES = ["sparse_mla_decode_indexer_amd/csrc/topk.hip", "sparse_mla_decode_indexer_amd/csrc/resolve.hip",
+                "sparse_mla_decode_indexer_amd/csrc/attention.hip", "sparse_mla_decode_indexer_amd/csrc/hs_internal.h",
+                "include/hisparse.h"]
+
+
 def source_sha256() -> str:
-    """Hash of the kernel sources, as recorded with the HBM byte counters."""
-    import glob
+    """Hash of the decode-step kernel sources, as recorded with the HBM byte counters."""
     import hashlib
-    src = sorted(glob.glob(os.path.join(ROOT, "sparse_mla_decode_indexer_amd", "csrc", "*")) +
-                 glob.glob(os.path.join(ROOT, "include", "*.h")))
+    src = sorted(os.path.join(ROOT, p) for p in STEP_SOURCES)
     h = hashlib.sha256()
     for p in src:
         h.update(os.path.relpath(p, ROOT).encode())
