@@ -70,3 +70,13 @@ def test_null_handles_rejected_without_device_work():
     assert L.hs_indexer_scores(None, None, None, None, 0, 64, None, 1, None, 0, None) == 1
     assert L.hs_destroy_pool(None) == 0
     assert B.status_string(2) == "exceeds pool capacity"
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    # no CPU fallback: without the built library every entry point fails loudly
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libhisparse.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        B.pool_requirements(desc())
