@@ -507,65 +507,109 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
   if (lse_out && d4 == 0) lse_out[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 
-// fp32 rows and queries: one workgroup per query row, vector-unit fp32.
-__global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q, int QR,
-                                                  const int32_t* __restrict__ plan, int K,
-                                                  const float* __restrict__ pool, int64_t pool_rows_n,
-                                                  float sm_scale, float* __restrict__ out,
-                                                  float* __restrict__ lse_out, uint32_t* __restrict__ err) {
+// fp32 rows and queries: one workgroup per query row, fp32 on the vector
+// units. Scores: wave w takes rows w, w + 4, ...; the 64 lanes read a row's
+// 576 values together (9 each, coalesced), 16 rows in flight per wave,
+// and sum across lanes. Weighted sum: thread t owns output dims t and
+// t + 256 and walks the rows in plan order, 32 rows' loads in flight;
+// absent rows read the zero row.
+constexpr int kF32Threads = 256;
+__global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restrict__ q, int QR,
+                                                         const int32_t* __restrict__ plan, int K,
+                                                         const float* __restrict__ pool, int64_t pool_rows_n,
+                                                         const float* __restrict__ zero_row, float sm_scale,
+                                                         float* __restrict__ out, float* __restrict__ lse_out,
+                                                         uint32_t* __restrict__ err) {
+  constexpr int kPerLane = kRowDim / 64;  // 9
+  constexpr int kWaves = kF32Threads / 64;
   __shared__ float qs[kRowDim];
   __shared__ float pb[kMaxTopK];
   __shared__ int pr_s[kMaxTopK];
-  __shared__ float red[4];
-  const int qh = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[kWaves];
+  const int qh = blockIdx.x, i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* qr = q + ((size_t)i * QR + qh) * kRowDim;
-  for (int d = tid; d < kRowDim; d += 256) qs[d] = qr[d];
-  __syncthreads();
-  float mx = -INFINITY;
-  for (int j = tid; j < K; j += 256) {
+  for (int d = tid; d < kRowDim; d += kF32Threads) qs[d] = qr[d];
+  for (int j = tid; j < K; j += kF32Threads) {
     int pr = plan[(size_t)i * K + j];
     if (pr >= pool_rows_n) {
       raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)j);
       pr = -1;
     }
     pr_s[j] = pr;
-    float s = -INFINITY;
-    if (pr >= 0) {
-      const float4* row = reinterpret_cast<const float4*>(pool + (size_t)pr * kRowDim);
-      float a = 0.f;
-      for (int d = 0; d < kRowDim / 4; ++d) {
-        const float4 x = row[d];
-        a += x.x * qs[4 * d] + x.y * qs[4 * d + 1] + x.z * qs[4 * d + 2] + x.w * qs[4 * d + 3];
-      }
-      s = a * sm_scale;
-    }
-    pb[j] = s;
-    mx = fmaxf(mx, s);
   }
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float qv[kPerLane];
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) qv[u] = qs[lane + 64 * u];
+  auto row_of = [&](int j) -> const float* {
+    const int pr = j < K ? pr_s[j] : -1;
+    return pr >= 0 ? pool + (size_t)pr * kRowDim : zero_row;
+  };
+
+  constexpr int kRowsInFlight = 16;
+  float mx = -INFINITY;
+  for (int j0 = wave; j0 < K; j0 += kWaves * kRowsInFlight) {
+    float x[kRowsInFlight][kPerLane];
+#pragma unroll
+    for (int r = 0; r < kRowsInFlight; ++r) {
+      const float* row = row_of(j0 + kWaves * r);
+#pragma unroll
+      for (int u = 0; u < kPerLane; ++u) x[r][u] = row[lane + 64 * u];
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsInFlight; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int u = 0; u < kPerLane; ++u) a += x[r][u] * qv[u];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+      const int j = j0 + kWaves * r;
+      if (j < K) {
+        const float sj = pr_s[j] >= 0 ? a * sm_scale : -INFINITY;
+        if (lane == 0) pb[j] = sj;
+        mx = fmaxf(mx, sj);
+      }
+    }
+  }
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) m = fmaxf(m, red[w]);
   __syncthreads();
   float sum = 0.f;
-  for (int j = tid; j < K; j += 256) {
+  for (int j = tid; j < K; j += kF32Threads) {
     const float p = pb[j] == -INFINITY ? 0.f : expf(pb[j] - m);
     pb[j] = p;
     sum += p;
   }
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  if (lane == 0) red[wave] = sum;
   __syncthreads();
-  const float l = red[0] + red[1] + red[2] + red[3];
-  float* dst = out + ((size_t)i * QR + qh) * kNope;
-  for (int d = tid; d < kNope; d += 256) {
-    float a = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const float p = pb[j];
-      if (p != 0.f) a += p * pool[(size_t)pr_s[j] * kRowDim + d];
+  float l = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) l += red[w];
+
+  constexpr int kPvInFlight = 32;
+  float a0 = 0.f, a1 = 0.f;  // dims tid and tid + 256
+  for (int j0 = 0; j0 < K; j0 += kPvInFlight) {
+    float v0[kPvInFlight], v1[kPvInFlight];
+#pragma unroll
+    for (int u = 0; u < kPvInFlight; ++u) {
+      const float* row = row_of(j0 + u);
+      v0[u] = row[tid];
+      v1[u] = row[tid + kF32Threads];
     }
-    dst[d] = l > 0.f ? a / l : 0.f;
+#pragma unroll
+    for (int u = 0; u < kPvInFlight; ++u) {
+      const float p = j0 + u < K ? pb[j0 + u] : 0.f;
+      a0 += p * v0[u];
+      a1 += p * v1[u];
+    }
   }
+  float* dst = out + ((size_t)i * QR + qh) * kNope;
+  dst[tid] = l > 0.f ? a0 / l : 0.f;
+  dst[tid + kF32Threads] = l > 0.f ? a1 / l : 0.f;
   if (lse_out && tid == 0) lse_out[(size_t)i * QR + qh] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
@@ -582,9 +626,9 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const int QR = q_per_req * n_heads;
   uint32_t* err = reinterpret_cast<uint32_t*>(p->state + p->lay.error);
   if (p->d.kv_dtype == HS_F32) {
-    k_attn_f32<<<dim3(QR, n_req), 256, 0, s>>>(static_cast<const float*>(q), QR, plan, K,
-                                                reinterpret_cast<const float*>(p->pool_rows),
-                                                p->pool_rows_n, sm_scale, out, lse_out, err);
+    k_attn_f32<<<dim3(QR, n_req), kF32Threads, 0, s>>>(
+        static_cast<const float*>(q), QR, plan, K, reinterpret_cast<const float*>(p->pool_rows), p->pool_rows_n,
+        reinterpret_cast<const float*>(p->state + p->off.zero_row), sm_scale, out, lse_out, err);
     HS_HIP_CHECK(hipGetLastError());
     return HS_OK;
   }

@@ -170,3 +170,41 @@ def test_indexer_full_size_sampled(R, maxc):
         assert pool.device_error()[0] == 0
     finally:
         pool.close()
+
+
+def test_indexer_scores_graph_replay_matches_eager():
+    """hs_indexer_scores captured in a hipGraph: every replay (with eager work
+    and synchronisations between replays) equals the eager result bit for bit."""
+    maxc = 4096
+    ctx = np.array([4096, 1000])
+    inp = W.IndexerInputs(404, 2, np.full(2, maxc), heads=32)
+    pool = _pool(2, maxc)
+    try:
+        ik = _setup(pool, inp, ctx)
+        req = torch.arange(2, dtype=torch.int32, device="cuda")
+        q, w = inp.next()
+        iq, iw = _bits_to_bf16(q).cuda(), torch.from_numpy(w).cuda()
+        eager = torch.zeros((2, maxc), dtype=torch.float32, device="cuda")
+        pool.indexer_scores(iq, iw, ik, req, eager)
+        torch.cuda.synchronize()
+        out = torch.zeros_like(eager)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            pool.indexer_scores(iq, iw, ik, req, out)  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            pool.indexer_scores(iq, iw, ik, req, out)
+        for rep in range(3):
+            out.fill_(-1.0)
+            _ = (eager * 2.0).sum().item()  # eager work between replays
+            g.replay()
+            torch.cuda.synchronize()
+            log(f"[indexer graph] replay {rep}")
+            assert torch.equal(out[0], eager[0]) and torch.equal(out[1, :1000], eager[1, :1000]), rep
+            assert torch.all(out[1, 1000:] == -1.0)
+        _check(eager.cpu().numpy()[1], q[1], w[1], inp.keys[1], 1000)
+    finally:
+        pool.close()
