@@ -65,6 +65,16 @@ def test_small_page_and_min_hot_buffer():
     run_steps(spec, 6)
 
 
+@pytest.mark.parametrize("base", ["single-128k", "single-1m-fp8"])
+@pytest.mark.parametrize("K,S", [(100, 256), (7, 64)])
+def test_ragged_top_k_through_the_step(base, K, S):
+    # a top-K that is not a multiple of the 32-row attention tile: the last
+    # tile of the plan is partly empty (100 = 3 x 32 + 4; 7 < 32), through
+    # top-K, resolve (misses, hits, LRU) and attention, bf16 and fp8 rows
+    scores = ("ar1", 0.9)
+    run_steps(small(base, ctx=6000, host_pages=60, top_k=K, hot_rows=S, scores=scores), 6)
+
+
 @pytest.mark.parametrize("K", [1, 7, 256, 2048])
 def test_topk_ties_and_sizes(K):
     rng = np.random.default_rng(K)
