@@ -363,17 +363,18 @@ def residency_probe(pool, buf, spec, pages_per_call: int = 64, calls: int = 4):
     part of a decode step): `calls` proactive-copy calls of `pages_per_call`
     complete GPU pages each into the pinned host store (PCIe device-to-host
     writes), enqueued back to back, then one release call under a budget of
-    half the GPU pages. HIP events on the stream the kernels run on; a large
-    device fill is enqueued first so that the host has queued the calls
-    before the first event is reached and the events time GPU work only."""
+    half the GPU pages. HIP events on the stream the kernels run on; a spin
+    kernel (~0.1 s) is enqueued first so that the host has queued every
+    launch of the calls before the first event is reached and the events
+    time GPU work only."""
     import torch
     R = spec.n_req
     dev = buf.req_ids.device
     stream = torch.cuda.current_stream()
-    filler = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
 
     def timed(fn):
-        filler.fill_(1.0)  # keeps the GPU busy while the host enqueues fn's launches
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e8))  # keeps the GPU busy while the host enqueues fn's launches
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -396,7 +397,6 @@ def residency_probe(pool, buf, spec, pages_per_call: int = 64, calls: int = 4):
     counts = torch.zeros(R, 2, dtype=torch.int32, device=dev)
     rel_ms = timed(lambda: pool.update_residency(buf.req_ids, budget, 0, 1024, freed, counts))
     released = int(counts[:, 1].sum().item())
-    del filler
     row_bytes = pool.row_bytes + (4 if spec.kv_dtype == "fp8" else 0)
     copied_bytes = copied * spec.page_size * row_bytes
     gbs = copied_bytes / (copy_ms * 1e-3) / 1e9 if copied else 0.0
