@@ -514,3 +514,80 @@ def test_imported_prefix_start_shared_host_rows():
         assert np.asarray(ref["counts"])[1][0] == 0  # request 1 never reads a resident row
     finally:
         rn.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_attention_plan_row_outside_pool_is_flagged_and_skipped(kv):
+    """A plan entry at or past the pool's row count raises HS_DEV_PLAN_RANGE
+    (first such entry: request position and plan index) and is treated as
+    absent: the output equals attention over the remaining rows."""
+    from oracle import bf16_decode, e4m3fn_decode
+    from gpu_helpers import ATTN_TOL, attn_rel_err
+    rng = np.random.default_rng(11)
+    K, H, n_rows = 256, 16, 1024
+    pool = TieredPool(page_size=64, num_pool_pages=n_rows // 64, max_requests=1, max_context=n_rows,
+                      kv_dtype=kv, top_k=K, hot_rows=512, max_batch=1, max_q_rows=H, host_rows=64)
+    try:
+        x = rng.standard_normal((n_rows, W.ROW_DIM)).astype(np.float32)
+        plan = rng.permutation(n_rows)[:K].astype(np.int32)
+        bad = 37
+        plan[bad] = n_rows + 5          # outside the pool
+        live = np.ones(K, dtype=bool)
+        live[bad] = False
+        q = rng.standard_normal((H, W.ROW_DIM)).astype(np.float32)
+        sm = 1.0 / np.sqrt(W.ROW_DIM)
+        if kv == "f32":
+            pool.pool_row_view().copy_(torch.from_numpy(x.view(np.uint8).reshape(n_rows, -1)).cuda())
+            logical = x.astype(np.float64)
+            qd = q.astype(np.float64)
+            d_q = torch.from_numpy(q).cuda().reshape(1, 1, H, W.ROW_DIM)
+        else:
+            if kv == "bf16":
+                bits = W.f32_to_bf16_bits(x)
+                pool.pool_row_view().copy_(torch.from_numpy(bits.view(np.uint8).reshape(n_rows, -1)).cuda())
+                logical = bf16_decode(bits)
+            else:
+                codes, sc = W.f32_rows_to_fp8(x)
+                pool.pool_row_view().copy_(torch.from_numpy(codes).cuda())
+                pool.pool_scales.copy_(torch.from_numpy(sc).cuda())
+                logical = e4m3fn_decode(codes) * sc[:, None].astype(np.float64)
+            qb = W.f32_to_bf16_bits(q)
+            qd = bf16_decode(qb)
+            d_q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16).reshape(1, 1, H, W.ROW_DIM)
+        d_plan = torch.from_numpy(plan).cuda().reshape(1, K)
+        out = torch.full((1, 1, H, W.NOPE_DIM), np.nan, device="cuda")
+        log(f"[gpu] plan row outside the pool, {kv}")
+        pool.sparse_mla_decode(d_q, d_plan, sm, out, None)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().reshape(H, -1)
+        o_ref, _ = mla_attention(qd, logical[plan[live]], sm)
+        assert attn_rel_err(o, o_ref) <= ATTN_TOL
+        err = pool.device_error()
+        assert err[0] == 3 and err[1] == 0 and err[2] == bad, err  # HS_DEV_PLAN_RANGE
+        pool.clear_device_error()
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
+
+
+def test_topk_request_id_outside_pool_is_flagged_and_padded():
+    """A req_ids entry outside [0, max_requests) raises HS_DEV_REQUEST_RANGE
+    and its top-K row is all -1; the other rows are unaffected."""
+    K, maxc = 64, 4096
+    pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=2, max_context=maxc, kv_dtype="bf16",
+                      top_k=K, hot_rows=64, max_batch=2, max_q_rows=16, host_rows=2 * maxc)
+    try:
+        rng = np.random.default_rng(5)
+        sc = rng.standard_normal((2, maxc)).astype(np.float32)
+        pool.set_residency(1, 3000, 0, None)
+        req = torch.tensor([7, 1], dtype=torch.int32, device="cuda")
+        idx = torch.full((2, K), -5, dtype=torch.int32, device="cuda")
+        log("[gpu] top-K with a request id outside the pool")
+        pool.select_topk(torch.from_numpy(sc).cuda(), req, idx)
+        got = idx.cpu().numpy()
+        assert np.all(got[0] == -1)
+        assert np.array_equal(got[1], select_topk(sc[1], 3000, K))
+        err = pool.device_error()
+        assert err[0] == 4 and err[1] == 0 and err[2] == 7, err  # HS_DEV_REQUEST_RANGE
+    finally:
+        pool.close()
