@@ -591,3 +591,27 @@ def test_topk_request_id_outside_pool_is_flagged_and_padded():
         assert err[0] == 4 and err[1] == 0 and err[2] == 7, err  # HS_DEV_REQUEST_RANGE
     finally:
         pool.close()
+
+
+def test_set_residency_page_id_outside_pool_becomes_host_only():
+    """A GPU page id at or past num_pool_pages given to set_residency raises
+    HS_DEV_PAGE_RANGE (request, logical page) and the page is recorded as
+    host-only: the following steps read its tokens from the host store and
+    match the oracle with that page on the host (state checked too)."""
+    spec = small("single-128k", ctx=6000, host_pages=60, top_k=256, hot_rows=512)
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        p = int(np.flatnonzero(wl.gpu_page[0] >= 0)[0])  # the oldest GPU page
+        bad = torch.tensor([rn.pool.desc.num_pool_pages + 3], dtype=torch.int32, device="cuda")
+        log(f"[gpu] set_residency with a page id outside the pool (logical page {p})")
+        rn.pool.set_residency(0, int(wl.ctx0[0]), int(wl.host_base[0]), bad, first_page=p)
+        torch.cuda.synchronize()
+        err = rn.pool.device_error()
+        assert err[0] == 2 and err[1] == 0 and err[2] == p, err  # HS_DEV_PAGE_RANGE
+        rn.pool.clear_device_error()
+        rn.oracle.set_pages(0, p, np.array([-1]))
+        for _ in range(4):
+            rn.step()
+    finally:
+        rn.close()
