@@ -119,3 +119,40 @@ def test_manager_copy_only_and_no_budget():
             assert moved[1] == 0
     finally:
         rn.close()
+
+
+def test_manager_call_replayed_from_a_graph():
+    """hs_update_residency captured in a hipGraph (a copy-only call of 8
+    pages): each replay, between eager decode steps, copies the next pages
+    exactly as the oracle's manager does, with every state word and host
+    copy checked after it."""
+    spec = small("single-128k", ctx=16384, host_pages=192)
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        _poison_gpu_pages_on_host(rn)
+        rn.step(heads=[0, 127])  # (the oracle takes the context length from its steps)
+        _update_and_check(rn, None, 8, 0, "eager call")  # loads the kernels outside capture
+        dev = rn.pool.device
+        counts = torch.zeros((1, 2), dtype=torch.int32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rn.pool.update_residency(rn.buf.req_ids, None, 8, 0, None, counts)
+        ps = spec.page_size
+        for rep in range(3):
+            rn.step(heads=[0, 127])
+            counts.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            ref = rn.oracle.update_residency(0, None, 8, 0)
+            c = counts.cpu().numpy()[0]
+            log(f"[gpu] residency graph replay {rep}: copied {c[0]}")
+            assert c.tolist() == [len(ref["copied"]), len(ref["demoted"])], f"replay {rep}: counts"
+            for p in ref["copied"]:
+                rows = wl.host_base[0] + p * ps + np.arange(ps)
+                assert np.array_equal(rn.pool.host_store[rows], rn.raw[rows]), f"replay {rep}: page {p}"
+            rn._check_state(f"replay {rep}")
+            assert rn.pool.device_error()[0] == 0
+        rn.step(heads=[0, 127])  # misses now read the copied rows
+    finally:
+        rn.close()
