@@ -36,8 +36,10 @@ import sys
 import time
 
 import numpy as np
+import faulthandler
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+faulthandler.enable(all_threads=True)  # a host crash prints every thread's Python stack
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published

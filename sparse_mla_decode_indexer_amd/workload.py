@@ -139,23 +139,47 @@ def row_bytes(kv_dtype: str) -> int:
 
 
 # ---------------------------------------------------------------- encodings
+# Pure numpy (no torch), so the row generator's worker threads call no
+# library with thread pools or lazy initialisation of its own. Both are
+# checked bit for bit against torch's conversions in the CPU tests.
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 to bf16 (RNE) and return the raw 16-bit patterns."""
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    """Round fp32 to bf16 (round to nearest, ties to even) and return the
+    raw 16-bit patterns (NaN -> the quiet NaN 0x7FC0 with its sign)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        r[nan] = ((u[nan] >> np.uint32(16)) & np.uint32(0x8000)).astype(np.uint16) | np.uint16(0x7FC0)
+    return r
+
+
+_FP8_MIN_NORMAL = np.float32(2.0 ** -6)
+
+
+def _e4m3fn_codes(y: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn codes of fp32 values with |y| <= 448, round to nearest,
+    ties to even. Normal results (|y| >= 2^-6) keep the fp32 exponent and
+    the top 3 mantissa bits after rounding the fp32 pattern at bit 20;
+    subnormal results are multiples of 2^-9, so their code is rint(|y|*2^9)
+    (0..8, where 8 is the smallest normal, code 0x08)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    a = np.abs(y)
+    u = a.view(np.uint32)
+    r = (u + (np.uint32(0x7FFFF) + ((u >> np.uint32(20)) & np.uint32(1)))) >> np.uint32(20)
+    normal = ((r >> np.uint32(3)) - np.uint32(120)) << np.uint32(3) | (r & np.uint32(7))
+    sub = np.rint(a * np.float32(512.0)).astype(np.uint32)
+    code = np.where(a < _FP8_MIN_NORMAL, sub, normal).astype(np.uint8)
+    return code | ((y.view(np.uint32) >> np.uint32(24)) & np.uint32(0x80)).astype(np.uint8)
 
 
 def f32_rows_to_fp8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Encode rows as OCP e4m3fn codes with one fp32 scale per row."""
-    import torch
     x = np.ascontiguousarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=1)
     scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0))
     scale = scale.astype(np.float32)
     y = np.clip(x / scale[:, None], -FP8_MAX, FP8_MAX).astype(np.float32)
-    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    return codes.copy(), scale
+    return _e4m3fn_codes(y), scale
 
 
 # ---------------------------------------------------------------- schedules

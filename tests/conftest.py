@@ -1,5 +1,9 @@
+import faulthandler
 import os
 import sys
+
+# a host crash prints every thread's Python stack
+faulthandler.enable(all_threads=True)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:

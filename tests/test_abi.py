@@ -80,3 +80,43 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
         B.lib()
     with pytest.raises(RuntimeError, match="missing"):
         B.pool_requirements(desc())
+
+
+def _declared_params():
+    """{function: [C parameter declarations]} parsed from include/hisparse.h."""
+    import re
+    text = open(B.HEADER).read()
+    out = {}
+    for m in re.finditer(r"^(?:hs_status|int32_t|const char\*)\s+(hs_\w+)\(([^)]*)\);", text, re.M):
+        params = [p.strip() for p in " ".join(m.group(2).split()).split(",")]
+        out[m.group(1)] = [] if params == ["void"] else params
+    return out
+
+
+def _ctype_for(decl: str):
+    """The ctypes type a C parameter declaration must be marshalled as."""
+    if "*" in decl or "[" in decl or decl.startswith("hipStream_t"):
+        return "pointer"
+    base = decl.rsplit(" ", 1)[0].replace("const ", "")
+    return {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "uint32_t": ctypes.c_uint32,
+            "size_t": ctypes.c_size_t, "float": ctypes.c_float, "hs_status": ctypes.c_int32}[base]
+
+
+def test_every_entry_point_has_matching_argtypes():
+    """ctypes passes an undeclared argument as a C int, which truncates a
+    64-bit pointer: every declared function is bound with argtypes whose
+    count and kinds match the header's parameter list."""
+    L = _lib()
+    decls = _declared_params()
+    assert set(decls) == set(B.header_functions())
+    for name, params in decls.items():
+        f = getattr(L, name)
+        assert f.argtypes is not None, name
+        assert len(f.argtypes) == len(params), (name, f.argtypes, params)
+        for decl, ct in zip(params, f.argtypes):
+            want = _ctype_for(decl)
+            if want == "pointer":
+                assert ct is ctypes.c_void_p or hasattr(ct, "contents") or issubclass(ct, ctypes.Array), \
+                    (name, decl, ct)
+            else:
+                assert ct is want, (name, decl, ct)

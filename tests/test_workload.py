@@ -85,3 +85,41 @@ def test_multi_layer_slots_share_contexts():
     assert not np.array_equal(wl.rows[a:a + 64], wl.rows[b:b + 64])
     with pytest.raises(ValueError):
         W.generate(small("batch32", n_req=5, layers=3, ctx_range=(3000, 9000), steps=1))
+
+
+def test_bf16_encoder_matches_torch():
+    """The generator's numpy bf16 rounding equals torch's fp32 -> bf16
+    conversion (round to nearest, ties to even) bit for bit, ties included."""
+    import torch
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(400_000) * np.exp(3 * rng.standard_normal(400_000))).astype(np.float32)
+    u = rng.integers(0, 1 << 16, size=20_000, dtype=np.uint32) << np.uint32(16)
+    ties = (u | np.uint32(0x8000)).view(np.float32)          # exactly halfway
+    near = (u | np.uint32(0x7FFF)).view(np.float32)
+    x = np.concatenate([x, ties, near, np.float32([0.0, -0.0, 3.3895314e38, -1e-45])])
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_bf16_bits(x), ref)
+
+
+def test_fp8_encoder_matches_torch():
+    """The generator's numpy e4m3fn rounding equals torch's fp32 ->
+    float8_e4m3fn conversion on every representable value, every midpoint
+    between neighbours (ties to even), their float32 neighbours, the
+    subnormal range and random values in [-448, 448]."""
+    import torch
+    codes = np.arange(0x7F, dtype=np.uint8)
+    v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    mids = ((v[:-1].astype(np.float64) + v[1:]) / 2).astype(np.float32)
+    c = np.concatenate([v, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e3))])
+    rng = np.random.default_rng(10)
+    c = np.concatenate([c, -c, np.float32([-0.0]), rng.uniform(-448, 448, 200_000).astype(np.float32),
+                        (rng.standard_normal(100_000) * 0.02).astype(np.float32)])
+    y = np.clip(c, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(W._e4m3fn_codes(y), ref)
+    x = (rng.standard_normal((64, 576)) * np.exp(rng.standard_normal(64))[:, None]).astype(np.float32)
+    codes8, scale = W.f32_rows_to_fp8(x)
+    dec = torch.from_numpy(codes8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.abs(dec).max(axis=1).tolist() == [448.0] * 64   # amax maps to the largest code
+    assert np.array_equal(scale, (np.abs(x).max(axis=1) / np.float32(448.0)).astype(np.float32))
