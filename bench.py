@@ -1,6 +1,12 @@
 """Benchmark: tiered sparse-MLA decode steps on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload single-128k]
+    python bench.py [--steps K] [--warmup W] [--workload batch32]
+
+The default workload is the largest one that fits one GPU: 32 concurrent
+requests with contexts uniform in [16K, 256K] tokens (bf16 latent rows,
+128 heads, top-K 2048, hot buffer 4096 rows, a third of the requests fully
+resident, a third with the newest quarter of their pages on the GPU, a third
+host-only), 28 timed + 4 warm-up steps = its 32 decode steps.
 
 Growing-context workloads (agent16, agent16-b) are timed with every
 request at its first step's context length.
@@ -24,6 +30,13 @@ tokens per request) with its algorithmic bytes (or FLOPs) per launch;
 committed counter summary profiles/decode_step_<workload>_hbm_traffic.json
 (null when absent or taken on other kernel sources).
 
+Measured denominators: before it touches the GPU, bench.py runs the probes
+of libhsprobe in a child process (python -m sparse_mla_decode_indexer_amd.probe):
+zero-copy coalesced reads of 512 MiB of pinned host memory (the PCIe
+host-read rate the miss copy is priced against beside the published link
+rate), a device copy and read (HBM), and a bf16 MFMA loop. A failure there
+leaves `measured_peaks` null and the published peaks in use.
+
 cpu_baseline: the CPU oracle (tests' reference, fp64 numpy) timed on a
 bounded prefix of the same steps on this host.
 """
@@ -32,6 +45,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -50,9 +64,10 @@ MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="single-128k")
+    ap.add_argument("--steps", type=int, default=28)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="batch32")
+    ap.add_argument("--no-probe", action="store_true", help="skip the measured-denominator probes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
@@ -74,6 +89,26 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
 
 
+def run_probes(timeout_s: int = 180):
+    """Measured denominators from libhsprobe, run in a child process (see the
+    module docstring). Returns the probe's JSON object, or None on failure."""
+    cmd = [sys.executable, "-u", "-m", "sparse_mla_decode_indexer_amd.probe"]
+    print("[bench] probes: PCIe host read, HBM copy/read, bf16 MFMA", file=sys.stderr, flush=True)
+    try:
+        r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        print("[bench] probes timed out; published peaks only", file=sys.stderr, flush=True)
+        return None
+    if r.returncode != 0:
+        print(f"[bench] probes failed (rc {r.returncode}); published peaks only\n{r.stderr[-2000:]}",
+              file=sys.stderr, flush=True)
+        return None
+    for line in reversed(r.stdout.splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    return None
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -84,6 +119,8 @@ def main():
               "and shard by request with no exchange, so a multi-GPU figure is not measured here.",
               file=sys.stderr)
         sys.exit(2)
+    probes = None if args.no_probe else run_probes()
+    pcie_meas = probes["pcie_host_read_gbs"] if probes else None
     import torch
 
     from sparse_mla_decode_indexer_amd import harness as Hn
@@ -218,9 +255,15 @@ def main():
             achieved = d["flops"] / (avg[dom] * 1e-6) / 1e12
         else:
             achieved = d["bytes"] / (avg[dom] * 1e-6) / 1e9
+        meas = None
+        if probes:
+            meas = {"pcie": probes["pcie_host_read_gbs"], "hbm": probes["hbm_read_gbs"],
+                    "mfma": probes["mfma_bf16_tflops"]}[d["bound"]]
         roof = {"kernel": name, "kernels": ENTRY_KERNELS[name], "bound": d["bound"],
                 "achieved": round(achieved, 2), "peak": d["peak"], "unit": d["unit"],
                 "frac": round(achieved / d["peak"], 4),
+                "measured_peak": meas,
+                "frac_of_measured": round(achieved / meas, 4) if meas else None,
                 "traffic": measured_traffic(spec.name, ENTRY_KERNELS[name]),
                 "avg_us": {n: round(float(a), 2) for n, a in zip(names, avg)},
                 "bytes_per_launch": {n: int(per[n]["bytes"]) for n in names},
@@ -243,6 +286,16 @@ def main():
         cold["pcie_bytes"] = int(mb)
         cold["resolve_pcie_gbs"] = round(mb / (cold["avg_us"]["resolve_rows"] * 1e-6) / 1e9, 2)
         cold["resolve_pcie_frac"] = round(cold["resolve_pcie_gbs"] / PCIE_PEAK_GBS, 4)
+        if pcie_meas:
+            cold["resolve_pcie_frac_of_measured"] = round(cold["resolve_pcie_gbs"] / pcie_meas, 4)
+    if roof is not None:
+        # the HBM target is read on the hit-only replay, the PCIe target on
+        # the steps with misses (timed steps and the cold step)
+        roof["hit_only_hbm_frac"] = hit["hbm_frac"] if hit else None
+        miss_gbs = b_pcie / (avg[1] * 1e-6) / 1e9 if b_pcie > 0 else None
+        roof["miss_pcie_gbs"] = round(miss_gbs, 2) if miss_gbs else None
+        roof["miss_pcie_frac_of_measured"] = round(miss_gbs / pcie_meas, 4) if (miss_gbs and pcie_meas) else None
+        roof["cold_pcie_frac_of_measured"] = cold.get("resolve_pcie_frac_of_measured") if cold else None
 
     resid = None if args.no_roofline else residency_probe(pool, buf, spec)
     indexer = None if args.no_roofline else indexer_probe(pool, buf, spec, wl)
@@ -253,6 +306,17 @@ def main():
 
     step_hbm = b_topk + b_resolve_hbm + b_attn
     value = 1e3 / ms_per_step
+    # roofline of the whole step: the slowest of its three resources at the
+    # published HBM and MFMA peaks and the measured PCIe host-read rate
+    pcie_den = pcie_meas or PCIE_PEAK_GBS
+    t_roof = max(step_hbm / (HBM_PEAK_GBS * 1e9), b_pcie / (pcie_den * 1e9),
+                 flops_attn / (MFMA_BF16_PEAK_TFS * 1e12))
+    step_roof = {"t_roof_us": round(t_roof * 1e6, 2), "t_step_us": round(ms_per_step * 1e3, 2),
+                 "frac": round(t_roof / (ms_per_step * 1e-3), 4),
+                 "pcie_denominator": "measured host read" if pcie_meas else "published link rate",
+                 "bound": ["hbm", "pcie", "mfma"][int(np.argmax([step_hbm / (HBM_PEAK_GBS * 1e9),
+                                                                 b_pcie / (pcie_den * 1e9),
+                                                                 flops_attn / (MFMA_BF16_PEAK_TFS * 1e12)]))]}
     line = {
         "metric": "sparse-MLA decode steps/s + top-K rows resolved/s; % of HBM/PCIe roofline",
         "value": round(value, 2),
@@ -279,7 +343,11 @@ def main():
         "resident_per_step": round(float(dc[0] / K), 1),
         "step_hbm_frac": round(step_hbm / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
         "step_pcie_frac": round(b_pcie / (ms_per_step * 1e-3) / 1e9 / PCIE_PEAK_GBS, 4),
+        "step_pcie_frac_of_measured": (round(b_pcie / (ms_per_step * 1e-3) / 1e9 / pcie_meas, 4)
+                                       if pcie_meas else None),
+        "step_roofline": step_roof,
         "roofline": roof,
+        "measured_peaks": probes,
         "cpu_baseline": cpu,
         "cold_step": cold,
         "hit_only_replay": hit,

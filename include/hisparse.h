@@ -88,7 +88,11 @@ enum {
   HS_DEV_INDEX_RANGE = 1,  /* a selected token >= the request's context length */
   HS_DEV_PAGE_RANGE = 2,   /* a page-table or hot-page id >= num_pool_pages */
   HS_DEV_PLAN_RANGE = 3,   /* an attention plan row >= the pool's row count */
-  HS_DEV_REQUEST_RANGE = 4 /* a req_ids entry outside [0, max_requests) */
+  HS_DEV_REQUEST_RANGE = 4, /* a req_ids entry outside [0, max_requests) */
+  HS_DEV_TIMEOUT = 5       /* a bounded wait inside hs_resolve_rows gave up (info: batch position and
+                              plan position of the copy wave, or 0xFFFFFFFF for the end-of-launch wait);
+                              the positions of that wave were not copied, so the plan of that call must
+                              not be used; the next call starts clean */
 };
 
 /* hs_set_residency flags */

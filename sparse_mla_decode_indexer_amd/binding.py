@@ -23,7 +23,7 @@ DTYPE_CODES = {"f32": HS_F32, "bf16": HS_BF16, "fp8": HS_FP8_E4M3}
 STATUS = {0: "HS_OK", 1: "HS_ERR_INVALID_ARGUMENT", 2: "HS_ERR_CAPACITY", 3: "HS_ERR_UNSUPPORTED",
           4: "HS_ERR_HIP", 5: "HS_ERR_OUT_OF_MEMORY", 6: "HS_ERR_DEVICE"}
 DEVICE_ERRORS = {0: "ok", 1: "index past context", 2: "page id outside pool",
-                 3: "plan row outside pool", 4: "request id out of range"}
+                 3: "plan row outside pool", 4: "request id out of range", 5: "bounded wait timed out"}
 
 
 class HsPoolDesc(ctypes.Structure):

@@ -3,7 +3,9 @@
     python -m sparse_mla_decode_indexer_amd.build
 
 Every .hip file under csrc/ is compiled to an object in _build/, then
-linked into sparse_mla_decode_indexer_amd/libhisparse.so.
+linked into sparse_mla_decode_indexer_amd/libhisparse.so (the decode path).
+The measurement probes under csrc/probe/ become libhsprobe.so, a library of
+their own that the decode path never loads.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhisparse.so")
+PROBE_LIB = os.path.join(PKG, "libhsprobe.so")
+PROBE_SRC = os.path.join(CSRC, "probe")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -39,12 +43,14 @@ EXTRA_FLAGS = {
 }
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d: str = CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    sub = os.path.basename(os.path.dirname(src))
+    stem = os.path.basename(src)[:-4]
+    obj = os.path.join(BUILD, (stem if sub == "csrc" else f"{sub}_{stem}") + ".o")
     cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -56,20 +62,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link both shared libraries; returns the
+    decode library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, psrcs = sources(), sources(PROBE_SRC)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

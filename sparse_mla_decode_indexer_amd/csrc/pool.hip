@@ -89,10 +89,10 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   of.tk_max = take(4 * B * max_chunks);
   of.tk_cand = take(8 * B * max_chunks * kTkChunk);
   of.tk_bound = take(4 * R);
-  of.rs_mdst = take(4 * B * (size_t)K);
+  of.rs_mdst = take(8 * B * (size_t)K);
   of.rs_mslot = take(4 * B * (size_t)K);
   of.rs_mold = take(4 * B * (size_t)K);
-  of.rs_ticket = take(8);
+  of.rs_ticket = take(16);
   of.ru_list = take(8 * B * (size_t)kRuMaxList);
   of.ru_ncopy = take(4 * B);
   of.at_part_rows = (int64_t)B * d->max_q_rows * kAttSplitCap;
@@ -288,7 +288,6 @@ hs_status hs_init_pool(const hs_pool_desc* desc, void* pool_rows, float* pool_sc
   fill(s8, lay.hot_pages, 4 * R * (sz.hot_rows / desc->page_size), 0xFFFFFFFFu, stream);
   fill(s8, lay.rev, 4 * R * (size_t)desc->max_context, 0xFFFFFFFFu, stream);
   fill(s8, lay.slot_tag, 4 * R * sz.hot_rows, 0xFFFFFFFFu, stream);
-  fill(s8, off.rs_mdst, 4 * (size_t)desc->max_batch * desc->top_k, 0x80000000u, stream);  // resolve: "pending"
   k_iota_rows<<<1024, 256, 0, stream>>>(reinterpret_cast<int32_t*>(s8 + lay.lru_order),
                                          desc->max_requests, sz.hot_rows);
   e = hipGetLastError();

@@ -11,16 +11,15 @@
 //     and rewrites the LRU order with ordered compactions in LDS, writes the
 //     plan and the counts, and for every plan position the hot slot and that
 //     slot's old token (misses) and last the copy destination: the pool row
-//     a miss is copied to, or -1;
+//     a miss is copied to, or -1, tagged with the launch's epoch;
 //   copy workgroup (request i, part c), one per 64 plan positions (4 per
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
 //     store over PCIe right away; each wave then waits until its four copy
 //     destinations are published, writes the rows the bookkeeper actually
 //     classified as misses into their hot slots (rows it did not guess are
-//     read then), moves the slots' tags and reverse-map entries from the old
-//     tokens to the new, and puts its destination entries back to "pending"
-//     for the next call. The guess only decides how early the PCIe reads
+//     read then) and moves the slots' tags and reverse-map entries from the
+//     old tokens to the new. The guess only decides how early the PCIe reads
 //     start; which rows are written comes from the bookkeeper.
 // Bookkeeper thread t owns plan positions t + 1024 e (e < P), so wave w
 // holds plan positions 1024 e + 64 w .. + 63 and the token-order rank of a
@@ -31,9 +30,19 @@
 // reverse-map lookups are scattered global loads.
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
-// bounded (a device error is raised past the bound and the copy skipped).
-// The destination entries start "pending" (pool initialisation) and are
-// left pending by their copy wave; the role tickets are left cleared.
+// bounded (HS_DEV_TIMEOUT is raised past the bound and the copy skipped).
+// Epochs. Every workgroup reads the launch sequence number before it takes
+// its ticket, and counts itself done at its end; the last workgroup to be
+// done advances the sequence and clears the ticket and done counters, so all
+// workgroups of one launch share one epoch, the next launch has another and
+// starts from cleared counters, and nothing waits for the end of a launch.
+// A destination entry is a 64-bit (epoch, pool row) pair, and a copy wave
+// takes an entry as published only when it carries its own launch's epoch.
+// An entry left from an earlier launch therefore never passes for this
+// launch's, even when that launch timed out before its copy waves read it,
+// and no entry has to be put back to "pending" after use. (The sequence is
+// 32 bits; an entry is rewritten by every launch that covers its batch
+// position, so only one unwritten for 2^32 - 1 launches could alias.)
 //
 // LRU order. lru_order lists all S slots in ascending (stamp, slot). With U
 // the slots hit this step and M misses, the victims are the first M slots of
@@ -52,10 +61,10 @@ namespace hs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RsScratch {
-  int32_t* mdst;                  // [batch][K] pool row a missed position is copied to, else -1
+  uint64_t* mdst;                 // [batch][K] (epoch << 32) | pool row a missed position is copied to, else -1
   int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
   int32_t* mold;                  // [batch][K] token that slot held before (or -1)
-  uint32_t* ticket;               // [0]: roles handed out ([1] unused)
+  uint32_t* ticket;               // [0]: roles handed out; [1]: launch sequence (epoch - 1); [2]: workgroups done
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
 
@@ -65,7 +74,13 @@ constexpr int kRsPos = kMaxTopK / kRsThreads;      // plan positions per bookkee
 constexpr int kRsSlots = kMaxHotRows / kRsThreads;  // LRU positions per bookkeeper thread, at most
 constexpr int kRsPart = 4 * kRsWaves;              // plan positions per copy workgroup
 constexpr int kSpinLimit = 1 << 20;                // polls of a destination (>= 0.1 s) before giving up
-constexpr int32_t kRsPending = INT32_MIN;          // copy destination not yet published
+constexpr uint32_t kRsSeqWrap = 0xFFFFFFFFu;        // sequence values 0 .. 2^32 - 2: epochs 1 .. 2^32 - 1
+
+// A published destination: the launch's epoch (never 0, the workspace's
+// initial value) above the pool row (or -1).
+__device__ __forceinline__ uint64_t rs_entry(uint32_t epoch, int32_t dst) {
+  return ((uint64_t)epoch << 32) | (uint32_t)dst;
+}
 
 struct RsArgs {
   const int32_t* idx;
@@ -88,6 +103,7 @@ struct RsStatic {
   int wmiss[kRsPos * kRsWaves];      // misses per (e, wave), then their exclusive prefix
   int n_res, n_hot;
   int role;
+  uint32_t epoch;
 };
 
 // Dynamic LDS of a bookkeeper, with Spad = 1024 Q >= S: lru[Spad] and
@@ -117,7 +133,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   // completed, so a copy wave that sees it also sees the rest. The LRU
   // state is written afterwards: no copy workgroup reads it.
   auto put = [](int32_t* p, int x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  int32_t* mdst = sc.mdst + (size_t)i * K;
+  const uint32_t epoch = st.epoch;
+  auto publish = [epoch](uint64_t* p, int32_t dst) {
+    __hip_atomic_store(p, rs_entry(epoch, dst), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint64_t* mdst = sc.mdst + (size_t)i * K;
   int32_t* mslot = sc.mslot + (size_t)i * K;
   int32_t* mold = sc.mold + (size_t)i * K;
   auto stores_done = []() {
@@ -135,7 +155,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       put(&mslot[j], -1);
     }
     stores_done();
-    for (int j = tid; j < K; j += kRsThreads) put(&mdst[j], -1);
+    for (int j = tid; j < K; j += kRsThreads) publish(&mdst[j], -1);
     return;
   }
   const int r = r0;
@@ -380,7 +400,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 #pragma unroll
   for (int e = 0; e < kRsPos; ++e) {
     const int j = e * kRsThreads + tid;
-    if (e < P && j < K) put(&mdst[j], ((missbits >> e) & 1u) && code[e] >= 0 ? code[e] : -1);
+    if (e < P && j < K) publish(&mdst[j], ((missbits >> e) & 1u) && code[e] >= 0 ? code[e] : -1);
   }
   // 5. LRU state: the untouched non-victims keep their order at the front,
   //    then the hit and victim slots in ascending slot number, all with
@@ -466,7 +486,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 // request i; wave w takes 4 of them.
 template <int ROW_BYTES, bool FP8>
 __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc,
-                                          int i, int c) {
+                                          int i, int c, uint32_t epoch) {
   constexpr int CH = ROW_BYTES / 16;   // 16-byte chunks per row
   constexpr int CPL = (CH + 63) / 64;  // chunks per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,26 +530,29 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   float scale = 0.f;
   if (FP8 && guess) scale = a.host_scales[hbase + t];
   // wait for the bookkeeper (each wave on its own): lanes 0..3 poll their
-  // positions' destinations with device-coherent loads until none is
-  // pending, then put them back to pending for the next call
+  // positions' destinations with device-coherent loads until each carries
+  // this launch's epoch
   const bool mine = lane < 4 && j0 + lane < K;
   const size_t jj = (size_t)i * K + j0 + (lane & 3);
   int md = -1;
   int spins = 0;
   for (;;) {
-    if (mine) md = __hip_atomic_load(&sc.mdst[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!__any(mine && md == kRsPending)) break;  // (loop condition uniform per wave)
+    bool pending = false;
+    if (mine) {
+      const uint64_t w = __hip_atomic_load(&sc.mdst[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pending = (uint32_t)(w >> 32) != epoch;
+      md = (int32_t)(uint32_t)w;
+    }
+    if (!__any(pending)) break;  // (loop condition uniform per wave)
     if (++spins > kSpinLimit) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if (spins > kSpinLimit) {  // (leave every entry pending, published or not)
-    if (mine) __hip_atomic_store(&sc.mdst[jj], kRsPending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, 0xFFFFFFFFu);
+  if (spins > kSpinLimit) {  // nothing of this wave's positions is written
+    if (lane == 0) raise_error(v.error, HS_DEV_TIMEOUT, (uint32_t)i, (uint32_t)j0);
     return;
   }
   int ms = -1, mo = -1;
   if (mine) {
-    __hip_atomic_store(&sc.mdst[jj], kRsPending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (md >= 0) {
       ms = __hip_atomic_load(&sc.mslot[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       mo = __hip_atomic_load(&sc.mold[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -577,7 +600,16 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   __shared__ RsStatic st;
   extern __shared__ __align__(16) unsigned char rs_dyn[];
   const int tid = threadIdx.x;
-  if (tid == 0) st.role = (int)atomicAdd(&sc.ticket[0], 1u);
+  if (tid == 0) {
+    const uint32_t seq = __hip_atomic_load(&sc.ticket[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the ticket is taken only after the sequence load has returned, so the
+    // sequence cannot advance before this workgroup has read it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    st.epoch = seq + 1u;
+    st.role = (int)atomicAdd(&sc.ticket[0], 1u);
+  }
   __syncthreads();
   const int role = st.role;
   if (role < a.n_req) {
@@ -585,20 +617,21 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   } else {
     const int q = role - a.n_req;
     const int i = q / sc.parts;
-    copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts);
+    copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts, st.epoch);
   }
-  // The workgroup with ticket 0 (a bookkeeper, done with its request)
-  // clears the ticket counter for the next launch once every workgroup has
-  // taken its ticket: a bounded wait for workgroups that only need resources
-  // to start, while no other workgroup waits for this one any more.
-  if (role == 0 && tid == 0) {
-    int spins = 0;
-    while (__hip_atomic_load(&sc.ticket[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
-      if (++spins > kSpinLimit) break;
-      __builtin_amdgcn_s_sleep(2);
+  // The last workgroup of the launch to finish (every other one has taken
+  // its ticket and read the sequence by then) prepares the next launch.
+  __syncthreads();
+  if (tid == 0) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    if (atomicAdd(&sc.ticket[2], 1u) == gridDim.x - 1) {
+      const uint32_t next = st.epoch == kRsSeqWrap ? 0u : st.epoch;  // sequence + 1, wrapped
+      __hip_atomic_store(&sc.ticket[1], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&sc.ticket[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&sc.ticket[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (spins > kSpinLimit) raise_error(v.error, HS_DEV_REQUEST_RANGE, 0u, 0xFFFFFFFEu);
-    __hip_atomic_store(&sc.ticket[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -612,7 +645,7 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
                          int32_t* plan_out, int32_t* counts_out, hipStream_t s) {
   StateView v = make_view(p);
   RsScratch sc;
-  sc.mdst = reinterpret_cast<int32_t*>(p->state + p->off.rs_mdst);
+  sc.mdst = reinterpret_cast<uint64_t*>(p->state + p->off.rs_mdst);
   sc.mslot = reinterpret_cast<int32_t*>(p->state + p->off.rs_mslot);
   sc.mold = reinterpret_cast<int32_t*>(p->state + p->off.rs_mold);
   sc.ticket = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);

@@ -82,12 +82,12 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
         B.pool_requirements(desc())
 
 
-def _declared_params():
-    """{function: [C parameter declarations]} parsed from include/hisparse.h."""
+def _declared_params(header=B.HEADER, prefix="hs_"):
+    """{function: [C parameter declarations]} parsed from a header."""
     import re
-    text = open(B.HEADER).read()
+    text = open(header).read()
     out = {}
-    for m in re.finditer(r"^(?:hs_status|int32_t|const char\*)\s+(hs_\w+)\(([^)]*)\);", text, re.M):
+    for m in re.finditer(r"^(?:hs_status|int32_t|const char\*)\s+(" + prefix + r"\w+)\(([^)]*)\);", text, re.M):
         params = [p.strip() for p in " ".join(m.group(2).split()).split(",")]
         out[m.group(1)] = [] if params == ["void"] else params
     return out
@@ -102,13 +102,28 @@ def _ctype_for(decl: str):
             "size_t": ctypes.c_size_t, "float": ctypes.c_float, "hs_status": ctypes.c_int32}[base]
 
 
-def test_every_entry_point_has_matching_argtypes():
+def _probe_lib():
+    from sparse_mla_decode_indexer_amd import probe as P
+    if not os.path.exists(P.LIB_PATH):
+        pytest.fail(f"{P.LIB_PATH} not built (run python -m sparse_mla_decode_indexer_amd.build)")
+    return P
+
+
+@pytest.mark.parametrize("which", ["hisparse", "hsprobe"])
+def test_every_entry_point_has_matching_argtypes(which):
     """ctypes passes an undeclared argument as a C int, which truncates a
     64-bit pointer: every declared function is bound with argtypes whose
     count and kinds match the header's parameter list."""
-    L = _lib()
-    decls = _declared_params()
-    assert set(decls) == set(B.header_functions())
+    if which == "hisparse":
+        L = _lib()
+        decls = _declared_params()
+        assert set(decls) == set(B.header_functions())
+    else:
+        P = _probe_lib()
+        L = P.lib()
+        decls = _declared_params(P.HEADER, "hsp_")
+        assert set(decls) == set(P.header_functions()) == set(P._SIGS)
+        assert len(decls) == 7
     for name, params in decls.items():
         f = getattr(L, name)
         assert f.argtypes is not None, name
