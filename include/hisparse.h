@@ -301,6 +301,26 @@ hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype,
                                const int32_t* plan, float sm_scale, float* out,
                                float* lse_out, hipStream_t stream);
 
+/* hs_sparse_mla_decode for callers that cannot allocate (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, results to rounding and errors, but the split partials of the
+ * attention kernels live in a fixed device array of the library, 16 MiB per
+ * GPU (8,176 partial rows of 512 fp32 values plus one fp32 each), held from
+ * the first hs_init_pool on that GPU until the process ends, instead of in
+ * the pool's workspace. The call allocates nothing (no hipMalloc, no
+ * allocating library routine). A batch whose smallest split needs more than
+ * 8,176 partial rows (n_req * q_per_req * n_heads * ceil(top_k / 2048) with
+ * top_k > 2048; with top_k <= 2048 no partials are needed) returns
+ * HS_ERR_CAPACITY and enqueues nothing. Every call on one GPU shares that
+ * GPU's array, so calls whose kernels overlap on one GPU (other streams,
+ * other pools, other threads) race; calls on one stream do not. The array
+ * needs no clearing: every partial a call reads was written by that call.
+ * The current device must be the pool's (else INVALID_ARGUMENT). */
+hs_status hs_sparse_mla_decode_noalloc(hs_pool* pool, const void* q, int32_t q_dtype,
+                                       int32_t n_req, int32_t q_per_req, int32_t n_heads,
+                                       const int32_t* plan, float sm_scale, float* out,
+                                       float* lse_out, hipStream_t stream);
+
 /* Residency manager ([P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载"
  * §"混合 HiSparse 的技术实现": fully resident requests have their completed
  * prefix pages copied to host memory ahead of need, hybrid requests keep

@@ -66,6 +66,7 @@ _SIGS = {
     "hs_resolve_rows": [_VP, _VP, _VP, _I32, _VP, _VP, _VP],
     "hs_update_residency": [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _VP],
     "hs_sparse_mla_decode": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
+    "hs_sparse_mla_decode_noalloc": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
     "hs_get_state_layout": [_VP, ctypes.POINTER(HsStateLayout)],
     "hs_get_device_error": [_VP, ctypes.POINTER(_U32 * 4), _VP],
     "hs_clear_device_error": [_VP, _VP],
@@ -168,6 +169,13 @@ def sparse_mla_decode(pool: int, q: int, q_dtype: int, n_req: int, q_per_req: in
     _check(lib().hs_sparse_mla_decode(pool, q, q_dtype, n_req, q_per_req, n_heads, plan,
                                       float(sm_scale), out, lse_out or None, stream or None),
            "hs_sparse_mla_decode")
+
+
+def sparse_mla_decode_noalloc(pool: int, q: int, q_dtype: int, n_req: int, q_per_req: int, n_heads: int,
+                              plan: int, sm_scale: float, out: int, lse_out: int, stream: int):
+    _check(lib().hs_sparse_mla_decode_noalloc(pool, q, q_dtype, n_req, q_per_req, n_heads, plan,
+                                              float(sm_scale), out, lse_out or None, stream or None),
+           "hs_sparse_mla_decode_noalloc")
 
 
 def get_state_layout(pool: int) -> HsStateLayout:

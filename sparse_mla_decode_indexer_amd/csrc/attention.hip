@@ -44,6 +44,8 @@
 // units, one workgroup per query row.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <math.h>
 #include <stdlib.h>
 
@@ -613,6 +615,27 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   if (lse_out && tid == 0) lse_out[(size_t)i * QR + qh] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+// Split partials of hs_sparse_mla_decode_noalloc (kStaticScratchBytes per
+// GPU, held until the process ends). Host code never uses this name as an
+// address: it uses the device address static_scratch_address returns.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hs_status static_scratch_address(int device, uint8_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* ptrs[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices || !out) return HS_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return set_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    ptrs[device] = static_cast<uint8_t*>(ptr);
+  }
+  *out = ptrs[device];
+  return HS_OK;
+}
+
 static int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
   return s ? atoi(s) : dflt;
@@ -620,7 +643,8 @@ static int env_int(const char* name, int dflt) {
 
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
                            int32_t q_per_req, int32_t n_heads, const int32_t* plan, float sm_scale,
-                           float* out, float* lse_out, hipStream_t s) {
+                           float* out, float* lse_out, float* part_o, float* part_lse, int64_t part_rows,
+                           hipStream_t s) {
   (void)q_dtype;
   const int K = p->d.top_k;
   const int QR = q_per_req * n_heads;
@@ -659,13 +683,13 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   if (tps > n_tiles) tps = n_tiles;
   if (tps > kAttMaxTilesPerSplit) tps = kAttMaxTilesPerSplit;
   int splits = (n_tiles + tps - 1) / tps;
-  while (splits > 1 && (int64_t)n_req * QR * splits > p->off.at_part_rows) {
+  while (splits > 1 && (int64_t)n_req * QR * splits > part_rows) {
     ++tps;
     splits = (n_tiles + tps - 1) / tps;
   }
-  if (tps > kAttMaxTilesPerSplit) return HS_ERR_CAPACITY;  // cannot happen for top_k <= 4096
-  float* part_o = reinterpret_cast<float*>(p->state + p->off.at_part_o);
-  float* part_lse = reinterpret_cast<float*>(p->state + p->off.at_part_lse);
+  // more tiles per workgroup than the kernel takes: the partial buffer is
+  // too small for this batch (nothing is enqueued)
+  if (tps > kAttMaxTilesPerSplit) return HS_ERR_CAPACITY;
   const float c2 = sm_scale * kLog2e;
   const dim3 grid(splits, n_req, n_hg);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);

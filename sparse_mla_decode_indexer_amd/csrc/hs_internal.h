@@ -33,6 +33,14 @@ constexpr int kRuMaxList = 1024;   // most pages copied or demoted per call
 constexpr int kAttSplitCap = 4;    // partial rows reserved per (request, query row)
 constexpr int kAttMinPartRows = 16384;  // at least this many partial rows (32 MiB)
 constexpr int kAttMaxTilesPerSplit = 64;
+// Split partials of hs_sparse_mla_decode_noalloc: a file-scope device array
+// of this many bytes (one per GPU the library runs on), holding
+// kStaticPartRows rows of 512 fp32 partial outputs followed by as many fp32
+// partial log-sum-exps.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int64_t kStaticPartRows = 8176;
+static_assert(kStaticPartRows * 4 * 512 % 256 == 0, "lse partials start 256-byte aligned");
+static_assert(kStaticPartRows * 4 * 513 <= (int64_t)kStaticScratchBytes, "partials fit the array");
 
 // ---------------------------------------------------------------- the handle
 struct Offsets {
@@ -57,6 +65,7 @@ struct hs_pool {
   uint8_t* pool_rows;         // device
   float* pool_scales;         // device (fp8) or null
   uint8_t* state;             // device workspace
+  uint8_t* static_scratch;    // device address of this device's no-alloc scratch array
   void* host_rows;            // pinned, mapped
   float* host_scales;         // pinned, mapped (fp8) or null
 };
@@ -101,9 +110,14 @@ hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_
 hs_status launch_indexer_scores(hs_pool* p, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
                                 int32_t n_heads, const int32_t* req_ids, int32_t n_req, float* scores,
                                 int64_t score_stride, hipStream_t s);
+// Split partials: part_o [part_rows][512] and part_lse [part_rows] fp32.
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
                            int32_t q_per_req, int32_t n_heads, const int32_t* plan,
-                           float sm_scale, float* out, float* lse_out, hipStream_t s);
+                           float sm_scale, float* out, float* lse_out, float* part_o,
+                           float* part_lse, int64_t part_rows, hipStream_t s);
+// Device address of the no-alloc scratch array on the current device
+// (resolved once per device; the device must be current).
+hs_status static_scratch_address(int device, uint8_t** out);
 
 // ---------------------------------------------------------------- device helpers
 // Sticky device error word: the first error wins; later ones are dropped.

@@ -265,6 +265,13 @@ hs_status hs_init_pool(const hs_pool_desc* desc, void* pool_rows, float* pool_sc
     delete p;
     return set_hip_error(e);
   }
+  // device address of this device's no-alloc scratch array (resolved once
+  // per device, with the device current)
+  st = static_scratch_address(p->device, &p->static_scratch);
+  if (st != HS_OK) {
+    delete p;
+    return st;
+  }
   // Pinned host store, mapped into the device address space so that the
   // resolve kernel reads single rows directly over PCIe.
   void* h = nullptr;
@@ -384,7 +391,32 @@ hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype, in
                   ((kv == HS_BF16 || kv == HS_FP8_E4M3) && q_dtype == HS_BF16);
   if (!ok) return HS_ERR_UNSUPPORTED;
   if (n_req == 0) return HS_OK;
-  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, sm_scale, out, lse_out, stream);
+  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, sm_scale, out, lse_out,
+                          reinterpret_cast<float*>(pool->state + pool->off.at_part_o),
+                          reinterpret_cast<float*>(pool->state + pool->off.at_part_lse), pool->off.at_part_rows,
+                          stream);
+}
+
+hs_status hs_sparse_mla_decode_noalloc(hs_pool* pool, const void* q, int32_t q_dtype, int32_t n_req,
+                                       int32_t q_per_req, int32_t n_heads, const int32_t* plan,
+                                       float sm_scale, float* out, float* lse_out, hipStream_t stream) {
+  if (!pool || !q || !plan || !out) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req < 0 || q_per_req < 1 || n_heads < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch) return HS_ERR_CAPACITY;
+  if ((int64_t)q_per_req * n_heads > pool->d.max_q_rows) return HS_ERR_CAPACITY;
+  const int kv = pool->d.kv_dtype;
+  const bool ok = (kv == HS_F32 && q_dtype == HS_F32) ||
+                  ((kv == HS_BF16 || kv == HS_FP8_E4M3) && q_dtype == HS_BF16);
+  if (!ok) return HS_ERR_UNSUPPORTED;
+  if (!pool->static_scratch) return HS_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  HS_HIP_CHECK(hipGetDevice(&dev));
+  if (dev != pool->device) return HS_ERR_INVALID_ARGUMENT;  // the scratch address is per device
+  if (n_req == 0) return HS_OK;
+  float* part_o = reinterpret_cast<float*>(pool->static_scratch);
+  float* part_lse = part_o + (size_t)kStaticPartRows * kNope;
+  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, sm_scale, out, lse_out, part_o,
+                          part_lse, kStaticPartRows, stream);
 }
 
 hs_status hs_get_state_layout(const hs_pool* pool, hs_state_layout* out) {

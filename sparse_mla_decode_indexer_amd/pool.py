@@ -126,6 +126,15 @@ class TieredPool:
         B.sparse_mla_decode(self.handle, q.data_ptr(), qd, n_req, q_per_req, n_heads, plan.data_ptr(),
                             sm_scale, out.data_ptr(), _ptr(lse), _stream())
 
+    def sparse_mla_decode_noalloc(self, q: torch.Tensor, plan: torch.Tensor, sm_scale: float,
+                                  out: torch.Tensor, lse: Optional[torch.Tensor] = None):
+        """sparse_mla_decode with its split partials in the library's fixed
+        per-GPU array instead of the pool workspace (allocates nothing)."""
+        n_req, q_per_req, n_heads, _ = q.shape
+        qd = B.HS_F32 if q.dtype == torch.float32 else B.HS_BF16
+        B.sparse_mla_decode_noalloc(self.handle, q.data_ptr(), qd, n_req, q_per_req, n_heads, plan.data_ptr(),
+                                    sm_scale, out.data_ptr(), _ptr(lse), _stream())
+
     def device_error(self):
         return B.get_device_error(self.handle, _stream())
 
