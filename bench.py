@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="batch32")
     ap.add_argument("--no-probe", action="store_true", help="skip the measured-denominator probes")
+    ap.add_argument("--group", type=int, default=-1,
+                    help="requests per group of the pipelined step (harness.PipelinedStep); -1, the "
+                         "default: the three entry points in sequence on one stream")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
@@ -142,6 +145,14 @@ def main():
     pool = Hn.make_pool(wl, device=dev)
     Hn.load_workload(pool, wl)
     buf = Hn.StepBuffers(wl, device=dev, n_steps=T)
+    group = args.group
+    if group > 0 and group < spec.n_req:
+        step_fn = Hn.PipelinedStep(pool, buf, group)
+    else:
+        group = -1
+
+        def step_fn(n):
+            Hn.decode_step(pool, buf, n)
     ss, qs = W.ScoreStream(wl), W.QueryStream(wl)
     host_scores, host_q = [], []
     for n in range(T):
@@ -171,14 +182,14 @@ def main():
         cold = timed_entry_points(pool, buf, [0])
         cold["misses"] = int(buf.counts[:, 2].sum().item())
     for n in range(1 if cold is not None else 0, Wm):
-        Hn.decode_step(pool, buf, n)
+        step_fn(n)
     torch.cuda.synchronize()
 
     # capture the K timed steps
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for n in range(Wm, T):
-            Hn.decode_step(pool, buf, n)
+            step_fn(n)
     torch.cuda.synchronize()
     snap_state = pool.state.clone()
     snap_rows = pool.pool_rows.clone()
@@ -333,6 +344,8 @@ def main():
         "config": {"workload": spec.name, "requests": R, "context": int(lens.max()),
                    "kv_dtype": spec.kv_dtype, "heads": spec.heads, "q_per_req": spec.q_per_req,
                    "top_k": Kt, "hot_rows": S, "residency": spec.residency,
+                   "step": (f"pipelined over groups of {group} requests on three streams"
+                            if group > 0 else "three entry points in sequence on one stream"),
                    **({"growth": "context frozen at the first step's length"}
                       if spec.growth is not None else {}),
                    **({"layers": spec.layers} if spec.layers > 1 else {})},

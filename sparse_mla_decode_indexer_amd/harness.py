@@ -6,7 +6,7 @@ calls select_topk -> resolve_rows -> sparse_mla_decode.
 """
 from __future__ import annotations
 
-from typing import Optional
+from typing import List, Optional
 
 import numpy as np
 import torch
@@ -119,3 +119,45 @@ def decode_step(pool: TieredPool, buf: StepBuffers, n: int = 0):
     pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
     pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
     pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)
+
+
+def request_groups(n_req: int, group: int) -> List[slice]:
+    """Consecutive batch positions in groups of `group` (the last one shorter)."""
+    return [slice(a, min(a + group, n_req)) for a in range(0, n_req, group)]
+
+
+class PipelinedStep:
+    """One decode step of a batch as a pipeline over groups of requests.
+
+    The three entry points run per group on three streams: top-K of group
+    g, then its resolve (which waits for that top-K), then its attention
+    (which waits for that resolve). Each entry point keeps its own stream,
+    so its calls stay in order (their scratch memory is indexed by batch
+    position), while the attention of group g overlaps the resolve (the
+    PCIe transfer of the missed rows) of group g + 1 and the top-K of later
+    groups. The step computes what decode_step computes; the calls fork from
+    and join back into the caller's current stream, so the whole step can be
+    captured in one hipGraph. Streams keep the default priority."""
+
+    def __init__(self, pool: TieredPool, buf: StepBuffers, group: int):
+        self.pool, self.buf = pool, buf
+        self.groups = request_groups(int(buf.req_ids.numel()), group)
+        self.streams = [torch.cuda.Stream(device=buf.req_ids.device) for _ in range(3)]
+
+    def __call__(self, n: int = 0):
+        pool, buf = self.pool, self.buf
+        s_tk, s_rs, s_at = self.streams
+        cur = torch.cuda.current_stream()
+        for st in self.streams:
+            st.wait_stream(cur)
+        for g in self.groups:
+            with torch.cuda.stream(s_tk):
+                pool.select_topk(buf.scores[n][g], buf.req_ids[g], buf.idx[g])
+            s_rs.wait_stream(s_tk)
+            with torch.cuda.stream(s_rs):
+                pool.resolve_rows(buf.idx[g], buf.req_ids[g], buf.plan[g], buf.counts[g])
+            s_at.wait_stream(s_rs)
+            with torch.cuda.stream(s_at):
+                pool.sparse_mla_decode(buf.q[n][g], buf.plan[g], buf.sm_scale, buf.out[g], buf.lse[g])
+        for st in self.streams:
+            cur.wait_stream(st)

@@ -366,6 +366,20 @@ class ScoreStream:
         self.n = 0
         self.shift_steps: List[int] = []
 
+    def planned_shift_steps(self, steps: int) -> List[int]:
+        """Steps n <= `steps` (counted from 1) at which the topic-shift draw
+        redraws every score, from a copy of the shift stream's state (the
+        stream itself is not advanced); [] without topic shifts."""
+        if self.proc[0] != "ar1_shift":
+            return []
+        g = np.random.Generator(np.random.PCG64())
+        g.bit_generator.state = self.shift_g.bit_generator.state
+        out = []
+        for n in range(max(self.n + 1, 2), steps + 1):
+            if g.random() < self.proc[2]:
+                out.append(n)
+        return out
+
     def next(self, lens: np.ndarray) -> np.ndarray:
         """Scores of the next step for context lengths `lens` [R]."""
         self.n += 1

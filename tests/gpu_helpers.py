@@ -13,9 +13,11 @@ oracle on the same seeded inputs:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 import sys
-from typing import Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 import torch
@@ -41,6 +43,56 @@ def make_oracle(wl: W.Workload) -> DecodeOracle:
                         sm_scale=wl.sm_scale)
 
 
+class ShardedOracle:
+    """The batch oracle run as one single-request DecodeOracle per request,
+    stepped in a thread pool (numpy's sorts and products release the GIL).
+    Requests share no state in the oracle, so every output is the one the
+    batched DecodeOracle.step gives; this only spreads the work over cores.
+    Exposes the attributes the tests read (hot, pages, gpu_page) and the
+    per-request calls (set_pages, update_residency, logical_rows)."""
+
+    def __init__(self, wl: W.Workload, threads: Optional[int] = None):
+        s = wl.spec
+        self.parts = [DecodeOracle(rows=wl.rows, scales=wl.scales, kv_dtype=s.kv_dtype,
+                                   host_base=[wl.host_base[r]], gpu_page=[wl.gpu_page[r]],
+                                   hot_pages=wl.hot_pages[r:r + 1], page_size=s.page_size, top_k=s.top_k,
+                                   hot_rows=s.hot_rows, ctx_capacity=[wl.ctx_final[r]], sm_scale=wl.sm_scale)
+                      for r in range(s.n_req)]
+        n = threads or min(16, len(os.sched_getaffinity(0)), s.n_req)
+        self.pool = cf.ThreadPoolExecutor(max_workers=max(1, n))
+
+    @property
+    def hot(self):
+        return [o.hot[0] for o in self.parts]
+
+    @property
+    def pages(self):
+        return [o.pages[0] for o in self.parts]
+
+    @property
+    def gpu_page(self):
+        return [o.gpu_page[0] for o in self.parts]
+
+    def set_pages(self, r, first_page, gpu_ids, host_copy_valid=False):
+        self.parts[r].set_pages(0, first_page, gpu_ids, host_copy_valid)
+
+    def update_residency(self, r, budget, max_copy, max_demote):
+        return self.parts[r].update_residency(0, budget, max_copy, max_demote)
+
+    def logical_rows(self, r, tokens):
+        return self.parts[r].logical_rows(0, tokens)
+
+    def step(self, scores, q, lens, with_attention=True) -> Dict[str, List[np.ndarray]]:
+        def one(r):
+            return self.parts[r].step(scores[r:r + 1], None if q is None else q[r:r + 1], [lens[r]],
+                                      with_attention=with_attention)
+        res = list(self.pool.map(one, range(len(self.parts))))
+        return {k: [x[k][0] for x in res] if res[0][k] else [] for k in res[0]}
+
+    def close(self):
+        self.pool.shutdown(wait=True)
+
+
 def q_f64(q: np.ndarray) -> np.ndarray:
     return bf16_decode(q) if q.dtype == np.uint16 else q.astype(np.float64)
 
@@ -52,16 +104,26 @@ def attn_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(num / np.maximum(den, 1e-30)))
 
 
+def attn_elem_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """Element-wise relative error, each element's denominator floored at
+    1e-3 of its row's largest magnitude (reported beside attn_rel_err)."""
+    den = np.maximum(np.abs(ref), 1e-3 * np.abs(ref).max(axis=-1, keepdims=True))
+    return float(np.max(np.abs(out - ref) / np.maximum(den, 1e-30)))
+
+
 class Runner:
     """One workload on one pool, stepped in lockstep with the oracle."""
 
-    def __init__(self, wl: W.Workload, check_state: bool = True):
+    def __init__(self, wl: W.Workload, check_state: bool = True, sharded: bool = False,
+                 group: Optional[int] = None):
         self.wl = wl
         self.spec = wl.spec
         self.pool = Hn.make_pool(wl)
         Hn.load_workload(self.pool, wl)
         self.buf = Hn.StepBuffers(wl)
-        self.oracle = make_oracle(wl)
+        # group: run each step as the pipelined step over groups of this many requests
+        self.pipe = Hn.PipelinedStep(self.pool, self.buf, group) if group else None
+        self.oracle = ShardedOracle(wl) if sharded else make_oracle(wl)
         self.scores = W.ScoreStream(wl)
         self.queries = W.QueryStream(wl)
         self.sched = W.context_schedule(self.spec, wl.ctx0, self.spec.steps)
@@ -69,6 +131,7 @@ class Runner:
         self.n = 0
         self.raw = Hn.store_bytes(wl)
         self.max_err = 0.0
+        self.max_elem_err = 0.0
         self.incremental = False          # growth sets only the new pages
         self.cur_len = np.asarray(wl.ctx0).copy()
 
@@ -89,7 +152,10 @@ class Runner:
         sc = self.scores.next(lens)
         q = self.queries.next()
         self.buf.upload(0, sc, q)
-        Hn.decode_step(self.pool, self.buf)
+        if self.pipe is not None:
+            self.pipe(0)
+        else:
+            Hn.decode_step(self.pool, self.buf)
         torch.cuda.synchronize()
         ref = self.oracle.step(sc, None, lens, with_attention=False)
         self.n += 1
@@ -107,20 +173,30 @@ class Runner:
         self._check_rows(idx, plan, tag)
         out = self.buf.out.cpu().numpy()
         lse = self.buf.lse.cpu().numpy()
-        qd = q_f64(q)
-        for r in range(s.n_req):
+        hs = list(range(s.heads)) if heads is None else list(heads)
+        qd = q_f64(q[:, :, hs])  # only the heads compared
+
+        def rows_of(r):
             toks = ref["idx"][r][ref["idx"][r] >= 0]
-            rows = self.oracle.logical_rows(r, toks)
-            hs = range(s.heads) if heads is None else heads
-            qr = qd[r][:, list(hs)].reshape(-1, W.ROW_DIM)
-            o_ref, l_ref = mla_attention(qr, rows, float(wl.sm_scale))
-            o = out[r][:, list(hs)].reshape(-1, W.NOPE_DIM)
-            l = lse[r][:, list(hs)].reshape(-1)
+            return self.oracle.logical_rows(r, toks)
+
+        # row decoding spreads over the oracle's threads; the products stay
+        # on this thread (BLAS called from many threads at once contends)
+        if isinstance(self.oracle, ShardedOracle):
+            all_rows = list(self.oracle.pool.map(rows_of, range(s.n_req)))
+        else:
+            all_rows = [rows_of(r) for r in range(s.n_req)]
+        for r in range(s.n_req):
+            rows = all_rows[r]
+            o_ref, l_ref = mla_attention(qd[r].reshape(-1, W.ROW_DIM), rows, float(wl.sm_scale))
+            o = out[r][:, hs].reshape(-1, W.NOPE_DIM)
+            l = lse[r][:, hs].reshape(-1)
             if rows.shape[0] == 0:
                 assert (o == 0).all() and np.isneginf(l).all(), tag
                 continue
             e = attn_rel_err(o, o_ref)
             self.max_err = max(self.max_err, e)
+            self.max_elem_err = max(self.max_elem_err, attn_elem_err(o, o_ref))
             assert e <= ATTN_TOL, f"{tag} req {r}: attention rel err {e:.3e}"
             le = float(np.max(np.abs(l - l_ref) / np.maximum(1.0, np.abs(l_ref))))
             assert le <= LSE_TOL, f"{tag} req {r}: lse err {le:.3e}"
@@ -158,6 +234,8 @@ class Runner:
 
     def close(self):
         self.pool.close()
+        if isinstance(self.oracle, ShardedOracle):
+            self.oracle.close()
 
 
 def small(name: str, **kw) -> W.WorkloadSpec:

@@ -615,3 +615,21 @@ def test_set_residency_page_id_outside_pool_becomes_host_only():
             rn.step()
     finally:
         rn.close()
+
+
+@pytest.mark.parametrize("group", [1, 3])
+def test_pipelined_step_over_request_groups(group):
+    """The step run as a pipeline over request groups on three streams
+    (top-K, resolve and attention of group g; attention of g overlapping the
+    resolve of g + 1) is bit-exact with the oracle like the sequential step:
+    7 requests of mixed residency in groups of 1 and 3 (the last group
+    shorter), cold and warm steps."""
+    spec = small("batch32", n_req=7, ctx_range=(4096, 40000), steps=4)
+    log(f"[gpu] pipelined step, groups of {group}")
+    wl = W.generate(spec)
+    rn = Runner(wl, group=group)
+    try:
+        for _ in range(4):
+            rn.step(heads=[0, 77])
+    finally:
+        rn.close()
