@@ -30,6 +30,7 @@ from .hisparse_oracle import (  # noqa: F401
     mla_attention,
     resolve_step,
     select_topk,
+    union_of_selections,
 )
 from .indexer import indexer_scores  # noqa: F401
 from .residency import PageState, update_residency  # noqa: F401

@@ -15,6 +15,12 @@ What one step computes, per request r (the pages' order):
      ([P3] §"稀疏MLA的核心思想" and its MLA note: K and V share one
      low-rank latent vector per token).
 
+Speculative steps (DecodeOracle.step_union): each query token of a request
+has its own indexer scores and top-K; the union of the selections is
+resolved once per step (one plan, one LRU update: the query tokens share the
+request's hot state, [P2] §"与 vLLM 栈的集成", speculative decoding), and each
+query token attends over its own selected rows only.
+
 Readings where the pages are silent (each listed in the design notes):
   * top-K ties go to the lower token index; the output lists the selected
     tokens in ascending index order, padded with -1 when L < K;
@@ -54,6 +60,27 @@ def select_topk(scores: np.ndarray, L: int, K: int) -> np.ndarray:
     out = np.full(K, -1, dtype=np.int64)
     out[:sel.size] = sel
     return out
+
+
+def union_of_selections(sels: Sequence[np.ndarray], capacity: int):
+    """Sorted union of several selections and where each selected token sits
+    in it (speculative decoding with one resolve per step: the resolve plan
+    of a step serves every query token of the request and they share its
+    hot state, [P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" §"与 vLLM 栈的集成").
+
+    sels: per query token, ascending token ids padded with -1. Returns
+    union [capacity] (the distinct tokens, ascending, -1 padded) and upos
+    [len(sels), K] (the union position of each selected token, -1 for
+    padding)."""
+    toks = sorted({int(x) for sel in sels for x in np.asarray(sel) if x >= 0})
+    if len(toks) > capacity:
+        raise ValueError("union larger than its capacity")
+    union = np.full(int(capacity), -1, dtype=np.int64)
+    union[:len(toks)] = toks
+    where = {x: i for i, x in enumerate(toks)}
+    upos = np.array([[where[int(x)] if x >= 0 else -1 for x in np.asarray(sel)] for sel in sels],
+                    dtype=np.int64)
+    return union, upos
 
 
 # --------------------------------------------------------------- row decode
@@ -241,6 +268,41 @@ class DecodeOracle:
         idx = self.host_base[r] + tokens
         sc = None if self.scales is None else self.scales[idx]
         return decode_rows(self.rows[idx], sc, self.kv_dtype)
+
+    def step_union(self, scores: np.ndarray, q: Optional[np.ndarray], lens: Sequence[int], k_per_token: int,
+                   with_attention: bool = True) -> Dict[str, list]:
+        """One speculative step: query token t of request r has its own
+        indexer scores scores[r][t] and its own top-k_per_token selection;
+        the union of a request's selections is resolved once (one plan, one
+        LRU update: the query tokens share the hot state) and each query
+        token attends over its own selected rows only. q [R, Q, H, 576]. The
+        union capacity is the oracle's top_k."""
+        R = len(lens)
+        out = {"sel": [], "union": [], "upos": [], "plan": [], "kind": [], "counts": [], "out": [], "lse": []}
+        for r in range(R):
+            self.pages[r].enter_context(self.prev_len[r], int(lens[r]), self.hot[r].step, self.ps)
+            self.prev_len[r] = int(lens[r])
+            Qn = scores[r].shape[0]
+            sels = [select_topk(scores[r][t], int(lens[r]), int(k_per_token)) for t in range(Qn)]
+            union, upos = union_of_selections(sels, self.K)
+            res = resolve_step(self.hot[r], union, self.gpu_page[r], self.hot_pages[r], self.ps)
+            self.pages[r].touch(union, self.hot[r].step, self.ps)
+            out["sel"].append(np.stack(sels))
+            out["union"].append(union)
+            out["upos"].append(upos)
+            for k in ("plan", "kind", "counts"):
+                out[k].append(res[k])
+            if with_attention:
+                qr = np.asarray(q[r], dtype=np.float64)
+                os_, ls_ = [], []
+                for t in range(Qn):
+                    toks = sels[t][sels[t] >= 0]
+                    o, lse = mla_attention(qr[t], self.logical_rows(r, toks), self.sm_scale)
+                    os_.append(o)
+                    ls_.append(lse)
+                out["out"].append(np.stack(os_))
+                out["lse"].append(np.stack(ls_))
+        return out
 
     def step(self, scores: np.ndarray, q: np.ndarray, lens: Sequence[int],
              with_attention: bool = True) -> Dict[str, np.ndarray]:

@@ -206,12 +206,15 @@ def brute_attention(qrows, kv, sm):
     return np.array(outs), np.array(lses)
 
 
-def brute_step(rq: BruteRequest, scores, L, K, rows, qrows, sm):
+def brute_step(rq: BruteRequest, scores, L, K, rows, qrows, sm, sel=None):
+    """One step of one request; `sel` (ascending tokens) replaces the top-K
+    of `scores` when given (the union of several selections)."""
     ps = rq.ps
     for p in range(-(-rq.length // ps), -(-L // ps)):
         rq.page_last[p] = rq.done          # entering pages take the count so far
     rq.length = L
-    sel = brute_topk(scores, L, K)
+    if sel is None:
+        sel = brute_topk(scores, L, K)
     rq.done += 1
     n = rq.done
     kind = {}
