@@ -124,7 +124,8 @@ typedef struct hs_pool_desc {
                              <= 8192 and a multiple of page_size */
   int32_t max_batch;      /* most requests in one per-step call, 1 .. max_requests */
   int32_t max_q_rows;     /* most q_per_req * n_heads in one sparse_mla_decode call */
-  int32_t reserved0;      /* must be 0 */
+  int32_t select_q;       /* most query tokens per request with a selection of their own
+                             (hs_select_topk_union): 0 or 1 (plain steps only) .. 8 */
   int64_t host_rows;      /* rows in the pinned host store, >= 1 */
 } hs_pool_desc;
 
@@ -230,6 +231,30 @@ hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_strid
                          const int32_t* req_ids, int32_t n_req, int32_t* idx_out,
                          hipStream_t stream);
 
+/* Top-K of a speculative step, one selection per query token, and their
+ * union ([P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" §"与 vLLM 栈的集成",
+ * speculative decoding: one resolve plan per step serves every query token
+ * of a request, which share its hot state). Query token t of request
+ * r = req_ids[i] has its own indexer scores and its own survivor bound.
+ *   scores     device fp32 [n_req][q_per_req][score_stride] (16-byte aligned,
+ *              score_stride >= max_context and a multiple of 4): row
+ *              i * q_per_req + t, valid over its first L_r entries
+ *   idx_out    device int32 [n_req][q_per_req][k_per_token]: the min(k, L_r)
+ *              selected tokens of each query token, as hs_select_topk
+ *   union_out  device int32 [n_req][top_k]: the distinct tokens of a
+ *              request's selections, ascending, -1 padded (the input of
+ *              hs_resolve_rows, whose plan then covers every query token)
+ *   upos_out   device int32 [n_req][q_per_req][k_per_token]: the union
+ *              position of each selected token (-1 for padding), the map
+ *              hs_sparse_mla_decode_union reads the plan through
+ * q_per_req <= select_q and q_per_req * k_per_token <= top_k (so every union
+ * fits). Errors: INVALID_ARGUMENT, CAPACITY; a request id out of range raises
+ * HS_DEV_REQUEST_RANGE and its rows are all -1. */
+hs_status hs_select_topk_union(hs_pool* pool, const float* scores, int64_t score_stride,
+                               const int32_t* req_ids, int32_t n_req, int32_t q_per_req,
+                               int32_t k_per_token, int32_t* idx_out, int32_t* union_out,
+                               int32_t* upos_out, hipStream_t stream);
+
 /* Indexer scores, the input of hs_select_topk ([P3] §"稀疏MLA的核心思想": the
  * indexer picks the tokens that enter attention; [P2] §"与 vLLM 栈的集成",
  * indexer KV item: the indexer keeps a per-token key cache of its own). The
@@ -320,6 +345,27 @@ hs_status hs_sparse_mla_decode_noalloc(hs_pool* pool, const void* q, int32_t q_d
                                        int32_t n_req, int32_t q_per_req, int32_t n_heads,
                                        const int32_t* plan, float sm_scale, float* out,
                                        float* lse_out, hipStream_t stream);
+
+/* Sparse MLA decode attention of a speculative step: query token t of
+ * request i attends over its own k_per_token selected rows only, read
+ * through the union's plan ([P3] "vLLM Hybrid HiSparse：稀疏MLA破解长上下文
+ * 显存瓶颈" §"稀疏MLA的核心思想": only the selected rows enter attention;
+ * [P2] §"与 vLLM 栈的集成": one plan per step).
+ *   q     device [n_req][q_per_req][n_heads][576] bf16 (fp32 for HS_F32 pools)
+ *   plan  device int32 [n_req][top_k]: hs_resolve_rows of union_out
+ *   upos  device int32 [n_req][q_per_req][k_per_token]: from
+ *         hs_select_topk_union; query token t reads plan row i at
+ *         upos[i][t][j] (-1 = absent)
+ *   out   device fp32 [n_req][q_per_req][n_heads][512], lse_out as
+ *         hs_sparse_mla_decode (per query token, over its own rows)
+ * A upos entry >= top_k raises HS_DEV_PLAN_RANGE and is treated as absent.
+ * Errors: INVALID_ARGUMENT, CAPACITY (n_req > max_batch, q_per_req * n_heads
+ * > max_q_rows or q_per_req * k_per_token > top_k), UNSUPPORTED. */
+hs_status hs_sparse_mla_decode_union(hs_pool* pool, const void* q, int32_t q_dtype,
+                                     int32_t n_req, int32_t q_per_req, int32_t n_heads,
+                                     const int32_t* plan, const int32_t* upos,
+                                     int32_t k_per_token, float sm_scale, float* out,
+                                     float* lse_out, hipStream_t stream);
 
 /* Residency manager ([P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载"
  * §"混合 HiSparse 的技术实现": fully resident requests have their completed

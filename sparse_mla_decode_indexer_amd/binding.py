@@ -32,7 +32,7 @@ class HsPoolDesc(ctypes.Structure):
                 ("nope_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("hot_rows", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("max_q_rows", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("max_q_rows", ctypes.c_int32), ("select_q", ctypes.c_int32),
                 ("host_rows", ctypes.c_int64)]
 
 
@@ -62,6 +62,8 @@ _SIGS = {
     "hs_host_rows": [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP)],
     "hs_set_residency": [_VP, _I32, _I32, _I64, _I32, _I32, _VP, _VP, _U32, _VP],
     "hs_select_topk": [_VP, _VP, _I64, _VP, _I32, _VP, _VP],
+    "hs_select_topk_union": [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP],
+    "hs_sparse_mla_decode_union": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _I32, _F32, _VP, _VP, _VP],
     "hs_indexer_scores": [_VP, _VP, _VP, _VP, _I64, _I32, _VP, _I32, _VP, _I64, _VP],
     "hs_resolve_rows": [_VP, _VP, _VP, _I32, _VP, _VP, _VP],
     "hs_update_residency": [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _VP],
@@ -143,6 +145,19 @@ def select_topk(pool: int, scores: int, score_stride: int, req_ids: int, n_req: 
                 stream: int):
     _check(lib().hs_select_topk(pool, scores, score_stride, req_ids, n_req, idx_out, stream or None),
            "hs_select_topk")
+
+
+def select_topk_union(pool: int, scores: int, score_stride: int, req_ids: int, n_req: int, q_per_req: int,
+                      k_per_token: int, idx_out: int, union_out: int, upos_out: int, stream: int):
+    _check(lib().hs_select_topk_union(pool, scores, score_stride, req_ids, n_req, q_per_req, k_per_token, idx_out,
+                                      union_out, upos_out, stream or None), "hs_select_topk_union")
+
+
+def sparse_mla_decode_union(pool: int, q: int, q_dtype: int, n_req: int, q_per_req: int, n_heads: int, plan: int,
+                            upos: int, k_per_token: int, sm_scale: float, out: int, lse_out: int, stream: int):
+    _check(lib().hs_sparse_mla_decode_union(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, upos, k_per_token,
+                                            float(sm_scale), out, lse_out or None, stream or None),
+           "hs_sparse_mla_decode_union")
 
 
 def indexer_scores(pool: int, iq: int, iw: int, ik: int, ik_stride: int, n_heads: int, req_ids: int,

@@ -154,12 +154,33 @@ __device__ inline float sum_across_kg(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The plan rows of query row group (request) i: plan[(i / div) * stride + j]
+// for j < K, or, with a union position map (speculative steps, where query
+// token t of a request reads its own selection through the union's plan),
+// plan[(i / div) * stride + upos[i * K + j]] (upos -1: absent).
+struct PlanRef {
+  const int32_t* plan;
+  const int32_t* upos;  // or null
+  int K, stride, div;
+};
+
+__device__ inline int plan_entry(const PlanRef& p, int i, int j, uint32_t* err) {
+  const int32_t* pl = p.plan + (size_t)(i / p.div) * p.stride;
+  if (!p.upos) return pl[j];
+  const int u = p.upos[(size_t)i * p.K + j];
+  if (u >= p.stride) {
+    raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)j);
+    return -1;
+  }
+  return u >= 0 ? pl[u] : -1;
+}
+
 // LDS chunk position of 16-byte chunk c of tile row r.
 __device__ inline int swz(int r, int c) { return r * kRowChunks + c; }
 
 template <bool FP8, int QB, bool BUF>
 __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
-    const uint16_t* __restrict__ q, int QR, const int32_t* __restrict__ plan, int K,
+    const uint16_t* __restrict__ q, int QR, PlanRef plan,
     const uint8_t* __restrict__ pool, const float* __restrict__ pool_scales, int64_t pool_rows_n,
     uint32_t pool_bytes, const uint8_t* __restrict__ zero_row, float c2, int tiles_per_split, int n_splits,
     float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ part_o,
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   const int qb = wave % QB, half = wave / QB;  // query block; key-dim half (QK) and value-dim half (PV)
   const int qh = hg * kQPerWG + qb * 16 + ln;
   const bool qvalid = qh < QR;
-  const int32_t* pl = plan + (size_t)i * K;
+  const int K = plan.K;
   const int n_tiles = (K + kTile - 1) / kTile;
   const int t_begin = sp * tiles_per_split;
   const int nt = min(n_tiles, t_begin + tiles_per_split) - t_begin;
@@ -200,7 +221,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // flight across the barrier and the first gathers
   for (int j = tid; j < nt * kTile; j += kAttThreads) {
     const int jj = t_begin * kTile + j;
-    int pr = jj < K ? pl[jj] : -1;
+    int pr = jj < K ? plan_entry(plan, i, jj, err) : -1;
     if (pr >= pool_rows_n) {
       raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)jj);
       pr = -1;
@@ -517,7 +538,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
 // absent rows read the zero row.
 constexpr int kF32Threads = 256;
 __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restrict__ q, int QR,
-                                                         const int32_t* __restrict__ plan, int K,
+                                                         PlanRef plan,
                                                          const float* __restrict__ pool, int64_t pool_rows_n,
                                                          const float* __restrict__ zero_row, float sm_scale,
                                                          float* __restrict__ out, float* __restrict__ lse_out,
@@ -528,11 +549,12 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   __shared__ float pb[kMaxTopK];
   __shared__ int pr_s[kMaxTopK];
   __shared__ float red[kWaves];
+  const int K = plan.K;
   const int qh = blockIdx.x, i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* qr = q + ((size_t)i * QR + qh) * kRowDim;
   for (int d = tid; d < kRowDim; d += kF32Threads) qs[d] = qr[d];
   for (int j = tid; j < K; j += kF32Threads) {
-    int pr = plan[(size_t)i * K + j];
+    int pr = plan_entry(plan, i, j, err);
     if (pr >= pool_rows_n) {
       raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)j);
       pr = -1;
@@ -642,16 +664,17 @@ static int env_int(const char* name, int dflt) {
 }
 
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
-                           int32_t q_per_req, int32_t n_heads, const int32_t* plan, float sm_scale,
-                           float* out, float* lse_out, float* part_o, float* part_lse, int64_t part_rows,
-                           hipStream_t s) {
+                           int32_t q_per_req, int32_t n_heads, const int32_t* plan, const int32_t* upos,
+                           int32_t k_plan, int32_t plan_div, float sm_scale, float* out, float* lse_out,
+                           float* part_o, float* part_lse, int64_t part_rows, hipStream_t s) {
   (void)q_dtype;
-  const int K = p->d.top_k;
+  const int K = k_plan;
+  const PlanRef pref{plan, upos, k_plan, p->d.top_k, plan_div};
   const int QR = q_per_req * n_heads;
   uint32_t* err = reinterpret_cast<uint32_t*>(p->state + p->lay.error);
   if (p->d.kv_dtype == HS_F32) {
     k_attn_f32<<<dim3(QR, n_req), kF32Threads, 0, s>>>(
-        static_cast<const float*>(q), QR, plan, K, reinterpret_cast<const float*>(p->pool_rows), p->pool_rows_n,
+        static_cast<const float*>(q), QR, pref, reinterpret_cast<const float*>(p->pool_rows), p->pool_rows_n,
         reinterpret_cast<const float*>(p->state + p->off.zero_row), sm_scale, out, lse_out, err);
     HS_HIP_CHECK(hipGetLastError());
     return HS_OK;
@@ -699,7 +722,7 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const bool buf = pool_bytes <= kBufMaxBytes;
   const uint32_t pb32 = buf ? (uint32_t)pool_bytes : 0u;
 #define HS_ATTN_LAUNCH(F, B, U)                                                                           \
-  k_attn_mfma<F, B, U><<<grid, 128 * (B), 0, s>>>(q16, QR, plan, K, p->pool_rows, sc, p->pool_rows_n, pb32, \
+  k_attn_mfma<F, B, U><<<grid, 128 * (B), 0, s>>>(q16, QR, pref, p->pool_rows, sc, p->pool_rows_n, pb32, \
                                                   zero_row, c2, tps, splits, out, lse_out, part_o, part_lse, err)
 #define HS_ATTN_LAUNCH_QB(F, U) \
   if (qb == 4)                  \

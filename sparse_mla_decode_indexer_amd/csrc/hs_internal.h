@@ -21,6 +21,7 @@ constexpr int kTkThreads = 256;
 constexpr int kTkBins = 4096;      // 12-bit radix digits
 constexpr int kTkMaxChunks = 2048; // => max_context <= 4,194,304
 constexpr int kTkStage = 8192;     // survivors staged in LDS by the select workgroup
+constexpr int kMaxSelectQ = 8;     // query tokens per request with a selection of their own
 
 // resolve
 constexpr int kRsThreads = 1024;
@@ -50,6 +51,7 @@ struct Offsets {
   size_t ru_list, ru_ncopy;  // residency manager: pages to copy [B][kRuMaxList][2], their count [B]
   size_t at_part_o, at_part_lse;
   int64_t at_part_rows;  // capacity of partial rows
+  int32_t sel_q;         // top-K scratch rows and survivor bounds per request (select_q, at least 1)
 };
 
 }  // namespace hs
@@ -100,8 +102,16 @@ hs_status set_hip_error(hipError_t e);
     if (e_ != hipSuccess) return hs::set_hip_error(e_); \
   } while (0)
 
+// Top-K of k tokens for each of the qsel score rows of each request (row
+// i * qsel + t of `scores` and of idx_out [n_req * qsel][k]); qsel = 1 and
+// k = top_k for a plain step.
 hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
-                      int32_t n_req, int32_t* idx_out, hipStream_t s);
+                      int32_t n_req, int32_t qsel, int32_t k, int32_t* idx_out, hipStream_t s);
+// Union of the qsel selections of each request (idx [n_req][qsel][k]):
+// union_out [n_req][top_k] ascending, -1 padded; upos_out [n_req][qsel][k]
+// the union position of each selected token (-1 for padding).
+hs_status launch_topk_union(hs_pool* p, const int32_t* idx, int32_t n_req, int32_t qsel, int32_t k,
+                            int32_t* union_out, int32_t* upos_out, hipStream_t s);
 hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
                          int32_t* plan_out, int32_t* counts_out, hipStream_t s);
 hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_req,
@@ -110,11 +120,14 @@ hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_
 hs_status launch_indexer_scores(hs_pool* p, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
                                 int32_t n_heads, const int32_t* req_ids, int32_t n_req, float* scores,
                                 int64_t score_stride, hipStream_t s);
-// Split partials: part_o [part_rows][512] and part_lse [part_rows] fp32.
+// Attention of n_req groups of q_per_req * n_heads query rows; group i reads
+// k_plan plan entries of plan row i / plan_div (rows of top_k entries),
+// through upos [n_req][k_plan] when given. Split partials: part_o
+// [part_rows][512] and part_lse [part_rows] fp32.
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
-                           int32_t q_per_req, int32_t n_heads, const int32_t* plan,
-                           float sm_scale, float* out, float* lse_out, float* part_o,
-                           float* part_lse, int64_t part_rows, hipStream_t s);
+                           int32_t q_per_req, int32_t n_heads, const int32_t* plan, const int32_t* upos,
+                           int32_t k_plan, int32_t plan_div, float sm_scale, float* out, float* lse_out,
+                           float* part_o, float* part_lse, int64_t part_rows, hipStream_t s);
 // Device address of the no-alloc scratch array on the current device
 // (resolved once per device; the device must be current).
 hs_status static_scratch_address(int device, uint8_t** out);

@@ -41,7 +41,8 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   if (d->kv_dtype != HS_F32 && d->kv_dtype != HS_BF16 && d->kv_dtype != HS_FP8_E4M3) return HS_ERR_UNSUPPORTED;
   if (d->top_k < 1 || d->top_k > kMaxTopK) return HS_ERR_INVALID_ARGUMENT;
   if (d->max_batch < 1 || d->max_batch > d->max_requests) return HS_ERR_INVALID_ARGUMENT;
-  if (d->max_q_rows < 1 || d->reserved0 != 0 || d->host_rows < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (d->max_q_rows < 1 || d->select_q < 0 || d->select_q > kMaxSelectQ || d->host_rows < 1)
+    return HS_ERR_INVALID_ARGUMENT;
   if ((int64_t)d->num_pool_pages * ps > (int64_t)INT32_MAX) return HS_ERR_CAPACITY;
   const int S = d->hot_rows == 0 ? 2 * d->top_k : d->hot_rows;
   if (S < d->top_k || S > kMaxHotRows) return HS_ERR_CAPACITY;
@@ -85,10 +86,12 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   Offsets of{};
   of.zero_row = take(4 * kRowDim);
   const size_t max_chunks = ((size_t)d->max_context + kTkChunk - 1) / kTkChunk;
-  of.tk_count = take(4 * B * max_chunks);
-  of.tk_max = take(4 * B * max_chunks);
-  of.tk_cand = take(8 * B * max_chunks * kTkChunk);
-  of.tk_bound = take(4 * R);
+  const size_t SQ = d->select_q > 1 ? (size_t)d->select_q : 1;  // score rows per request
+  of.sel_q = (int32_t)SQ;
+  of.tk_count = take(4 * B * SQ * max_chunks);
+  of.tk_max = take(4 * B * SQ * max_chunks);
+  of.tk_cand = take(8 * B * SQ * max_chunks * kTkChunk);
+  of.tk_bound = take(4 * R * SQ);
   of.rs_mdst = take(8 * B * (size_t)K);
   of.rs_mslot = take(4 * B * (size_t)K);
   of.rs_mold = take(4 * B * (size_t)K);
@@ -354,7 +357,23 @@ hs_status hs_select_topk(hs_pool* pool, const float* scores, int64_t score_strid
   if (score_stride < pool->d.max_context || (score_stride & 3)) return HS_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(scores) & 15) return HS_ERR_INVALID_ARGUMENT;
   if (n_req == 0) return HS_OK;
-  return launch_topk(pool, scores, score_stride, req_ids, n_req, idx_out, stream);
+  return launch_topk(pool, scores, score_stride, req_ids, n_req, 1, pool->d.top_k, idx_out, stream);
+}
+
+hs_status hs_select_topk_union(hs_pool* pool, const float* scores, int64_t score_stride,
+                               const int32_t* req_ids, int32_t n_req, int32_t q_per_req,
+                               int32_t k_per_token, int32_t* idx_out, int32_t* union_out,
+                               int32_t* upos_out, hipStream_t stream) {
+  if (!pool || !scores || !req_ids || !idx_out || !union_out || !upos_out) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req < 0 || q_per_req < 1 || k_per_token < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch || q_per_req > pool->off.sel_q) return HS_ERR_CAPACITY;
+  if ((int64_t)q_per_req * k_per_token > pool->d.top_k) return HS_ERR_CAPACITY;
+  if (score_stride < pool->d.max_context || (score_stride & 3)) return HS_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(scores) & 15) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req == 0) return HS_OK;
+  hs_status st = launch_topk(pool, scores, score_stride, req_ids, n_req, q_per_req, k_per_token, idx_out, stream);
+  if (st != HS_OK) return st;
+  return launch_topk_union(pool, idx_out, n_req, q_per_req, k_per_token, union_out, upos_out, stream);
 }
 
 hs_status hs_indexer_scores(hs_pool* pool, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
@@ -391,8 +410,8 @@ hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype, in
                   ((kv == HS_BF16 || kv == HS_FP8_E4M3) && q_dtype == HS_BF16);
   if (!ok) return HS_ERR_UNSUPPORTED;
   if (n_req == 0) return HS_OK;
-  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, sm_scale, out, lse_out,
-                          reinterpret_cast<float*>(pool->state + pool->off.at_part_o),
+  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, nullptr, pool->d.top_k, 1, sm_scale,
+                          out, lse_out, reinterpret_cast<float*>(pool->state + pool->off.at_part_o),
                           reinterpret_cast<float*>(pool->state + pool->off.at_part_lse), pool->off.at_part_rows,
                           stream);
 }
@@ -415,8 +434,31 @@ hs_status hs_sparse_mla_decode_noalloc(hs_pool* pool, const void* q, int32_t q_d
   if (n_req == 0) return HS_OK;
   float* part_o = reinterpret_cast<float*>(pool->static_scratch);
   float* part_lse = part_o + (size_t)kStaticPartRows * kNope;
-  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, sm_scale, out, lse_out, part_o,
-                          part_lse, kStaticPartRows, stream);
+  return launch_attention(pool, q, q_dtype, n_req, q_per_req, n_heads, plan, nullptr, pool->d.top_k, 1, sm_scale,
+                          out, lse_out, part_o, part_lse, kStaticPartRows, stream);
+}
+
+hs_status hs_sparse_mla_decode_union(hs_pool* pool, const void* q, int32_t q_dtype, int32_t n_req,
+                                     int32_t q_per_req, int32_t n_heads, const int32_t* plan,
+                                     const int32_t* upos, int32_t k_per_token, float sm_scale, float* out,
+                                     float* lse_out, hipStream_t stream) {
+  if (!pool || !q || !plan || !upos || !out) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req < 0 || q_per_req < 1 || n_heads < 1 || k_per_token < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch) return HS_ERR_CAPACITY;
+  if ((int64_t)q_per_req * n_heads > pool->d.max_q_rows) return HS_ERR_CAPACITY;
+  if ((int64_t)q_per_req * k_per_token > pool->d.top_k) return HS_ERR_CAPACITY;
+  const int kv = pool->d.kv_dtype;
+  const bool ok = (kv == HS_F32 && q_dtype == HS_F32) ||
+                  ((kv == HS_BF16 || kv == HS_FP8_E4M3) && q_dtype == HS_BF16);
+  if (!ok) return HS_ERR_UNSUPPORTED;
+  if (n_req == 0) return HS_OK;
+  // query token t of request i is query row group i * q_per_req + t: its
+  // n_heads rows ([n_req][q_per_req][n_heads][576] is [n_req * q_per_req]
+  // [n_heads][576]) read the union plan row i through upos row i * q_per_req + t
+  return launch_attention(pool, q, q_dtype, n_req * q_per_req, 1, n_heads, plan, upos, k_per_token, q_per_req,
+                          sm_scale, out, lse_out, reinterpret_cast<float*>(pool->state + pool->off.at_part_o),
+                          reinterpret_cast<float*>(pool->state + pool->off.at_part_lse), pool->off.at_part_rows,
+                          stream);
 }
 
 hs_status hs_get_state_layout(const hs_pool* pool, hs_state_layout* out) {

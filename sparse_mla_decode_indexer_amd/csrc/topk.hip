@@ -8,9 +8,10 @@
 // (K - #{key > T}) tokens with key T in token order, where T is the exact
 // K-th largest key.
 //
-// Two kernels per call:
+// Two kernels per call (each score row is one request's, or, for a
+// speculative step, one query token's of a request, with a bound of its own):
 //   k_topk_filter  workgroup (c, i) reads scores [2048c, 2048c + 2048) of
-//                  request i, keeps every key >= the request's bound, in
+//                  score row i, keeps every key >= the row's bound, in
 //                  token order, in its slice of a candidate buffer (ballot
 //                  ranks, no LDS tables, no atomics) and writes the slice's
 //                  count and largest key. Many small workgroups per CU.
@@ -38,11 +39,13 @@ constexpr int kTkSelThreads = 1024;
 constexpr int kTkSelWaves = kTkSelThreads / 64;
 
 struct TkScratch {
-  int32_t* count;   // [batch][max_chunks] survivors per chunk
-  uint32_t* maxk;   // [batch][max_chunks] largest surviving key per chunk
-  uint2* cand;      // [batch][max_chunks * kTkChunk] (key, token), chunk slices
-  uint32_t* bound;  // [max_requests] survivor bound for the next call
+  int32_t* count;   // [score rows][max_chunks] survivors per chunk
+  uint32_t* maxk;   // [score rows][max_chunks] largest surviving key per chunk
+  uint2* cand;      // [score rows][max_chunks * kTkChunk] (key, token), chunk slices
+  uint32_t* bound;  // [max_requests][bound_q] survivor bound for the next call
   int32_t max_chunks;
+  int32_t qsel;     // score rows per request in this call (row i * qsel + t)
+  int32_t bound_q;  // bounds per request (the pool's select_q, at least 1)
 };
 
 __device__ inline uint32_t score_key(float f) {
@@ -74,21 +77,22 @@ __device__ inline int wave_incl_sum(int x) {
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_filter(const float* __restrict__ scores, int64_t stride,
                                                             const int32_t* __restrict__ req_ids, StateView v,
-                                                            TkScratch sc) {
+                                                            TkScratch sc, int K) {
   constexpr int NW = kTkThreads / 64;
   constexpr int PER_WAVE = kTkChunk / NW;  // 512 scores per wave
   constexpr int NU = PER_WAVE / 256;       // float4 loads per lane
   __shared__ int wcount[NW];
   __shared__ uint32_t wmax[NW];
   const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = request_of(req_ids, i, v);
+  const int qi = i / sc.qsel, qt = i - qi * sc.qsel;  // request position, query token
+  const int r = request_of(req_ids, qi, v);
   if (r < 0) return;
   const int L = v.ctx_len[r];
-  if (L <= v.top_k) return;
+  if (L <= K) return;
   const int nch = (L + kTkChunk - 1) / kTkChunk;
   if (c >= nch) return;
   const float* s = scores + (size_t)i * stride;
-  const uint32_t thr = sc.bound[r];
+  const uint32_t thr = sc.bound[(size_t)r * sc.bound_q + qt];
   const int beg = c * kTkChunk + wave * PER_WAVE, end = min(L, beg + PER_WAVE);
   float4 x[NU];
 #pragma unroll
@@ -200,7 +204,7 @@ __device__ void hist_find2(const uint32_t* h, int need0, int need1, int* wtot, F
 
 __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __restrict__ scores, int64_t stride,
                                                                const int32_t* __restrict__ req_ids, StateView v,
-                                                               TkScratch sc, int32_t* __restrict__ idx_out) {
+                                                               TkScratch sc, int K, int32_t* __restrict__ idx_out) {
   constexpr int NW = kTkSelWaves;
   __shared__ __align__(16) uint32_t hist[3][kTkBins];
   __shared__ int off[kTkMaxChunks + 1];
@@ -211,11 +215,11 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   __shared__ uint32_t wmax[NW];
   __shared__ FindOut fres;
   const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = v.top_k;
+  const int qi = i / sc.qsel, qt = i - qi * sc.qsel;  // request position, query token
   int32_t* out = idx_out + (size_t)i * K;
-  const int r = request_of(req_ids, i, v);
+  const int r = request_of(req_ids, qi, v);
   if (r < 0) {
-    if (tid == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)i, (uint32_t)req_ids[i]);
+    if (tid == 0) raise_error(v.error, HS_DEV_REQUEST_RANGE, (uint32_t)qi, (uint32_t)req_ids[qi]);
     for (int j = tid; j < K; j += kTkSelThreads) out[j] = -1;
     return;
   }
@@ -229,7 +233,8 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
   const uint2* cand = sc.cand + (size_t)i * sc.max_chunks * kTkChunk;
   const int32_t* cnt = sc.count + (size_t)i * sc.max_chunks;
   const uint32_t* cmx = sc.maxk + (size_t)i * sc.max_chunks;
-  const uint32_t thr = sc.bound[r];
+  uint32_t* bound = sc.bound + (size_t)r * sc.bound_q + qt;
+  const uint32_t thr = *bound;
 
   // Speculative preload (contexts of up to NW * kPreSlots chunks): the
   // first 64 * kPreU survivors of each of this wave's chunks (chunks wave,
@@ -510,12 +515,12 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
       const uint32_t d = (T - base) + (1u << s1);
       nb = base > d ? base - d : 0u;
     }
-    sc.bound[r] = nb;
+    *bound = nb;
   }
 }
 
 hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
-                      int32_t n_req, int32_t* idx_out, hipStream_t s) {
+                      int32_t n_req, int32_t qsel, int32_t k, int32_t* idx_out, hipStream_t s) {
   StateView v = make_view(p);
   TkScratch sc;
   sc.count = reinterpret_cast<int32_t*>(p->state + p->off.tk_count);
@@ -523,8 +528,103 @@ hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int
   sc.cand = reinterpret_cast<uint2*>(p->state + p->off.tk_cand);
   sc.bound = reinterpret_cast<uint32_t*>(p->state + p->off.tk_bound);
   sc.max_chunks = (p->d.max_context + kTkChunk - 1) / kTkChunk;
-  k_topk_filter<<<dim3(sc.max_chunks, n_req), kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc);
-  k_topk_select<<<n_req, kTkSelThreads, 0, s>>>(scores, stride, req_ids, v, sc, idx_out);
+  sc.qsel = qsel;
+  sc.bound_q = p->off.sel_q;
+  const int rows = n_req * qsel;
+  k_topk_filter<<<dim3(sc.max_chunks, rows), kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc, k);
+  k_topk_select<<<rows, kTkSelThreads, 0, s>>>(scores, stride, req_ids, v, sc, k, idx_out);
+  HS_HIP_CHECK(hipGetLastError());
+  return HS_OK;
+}
+
+// Union of the selections of a request's query tokens (one workgroup per
+// request). Each selection is ascending with its valid entries first. An
+// entry is the owner of its token when no earlier list holds the token, so
+// every distinct token has one owner; the union position of a token x is the
+// number of distinct tokens below x, the sum over the lists of their owners
+// below x: an exclusive count of owners in list order, read at each list's
+// lower bound of x. Owners write the union; every entry writes its position.
+constexpr int kUnThreads = 1024;
+constexpr int kUnRounds = kMaxTopK / kUnThreads;
+
+__global__ __launch_bounds__(kUnThreads) void k_topk_union(const int32_t* __restrict__ idx, int qsel, int K, int cap,
+                                                           int32_t* __restrict__ union_out,
+                                                           int32_t* __restrict__ upos_out) {
+  __shared__ int lst[kMaxTopK];
+  __shared__ int opre[kMaxTopK + 1];
+  __shared__ int mcount[kMaxSelectQ];
+  __shared__ int wtot[kUnThreads / 64 + 1];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int n = qsel * K;  // <= cap <= kMaxTopK
+  const int32_t* src = idx + (size_t)i * n;
+  for (int x = tid; x < n; x += kUnThreads) lst[x] = src[x];
+  if (tid < kMaxSelectQ) mcount[tid] = 0;
+  __syncthreads();
+  for (int x = tid; x < n; x += kUnThreads)
+    if (lst[x] >= 0) atomicAdd(&mcount[x / K], 1);
+  __syncthreads();
+  int lbs[kUnRounds][kMaxSelectQ];  // lower bound of each entry's token in every list
+  bool own[kUnRounds];
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < kUnRounds; ++e) {
+    own[e] = false;
+    const int x = e * kUnThreads + tid;
+    if (e * kUnThreads < n) {  // uniform
+      if (x < n) {
+        const int t = x / K, j = x - t * K;
+        const int tok = lst[x];
+        if (j < mcount[t]) {
+          own[e] = true;
+#pragma unroll
+          for (int q = 0; q < kMaxSelectQ; ++q) {
+            if (q < qsel) {
+              int lo = 0, hi = mcount[q];
+              if (q == t) {
+                lo = j;
+              } else {
+                while (lo < hi) {
+                  const int mid = (lo + hi) >> 1;
+                  if (lst[q * K + mid] < tok) lo = mid + 1; else hi = mid;
+                }
+                if (q < t && lo < mcount[q] && lst[q * K + lo] == tok) own[e] = false;
+              }
+              lbs[e][q] = lo;
+            }
+          }
+        }
+      }
+      int tot;
+      const int pre = block_excl_count(own[e], wtot, tot);
+      if (x < n) opre[x] = base + pre;
+      base += tot;
+    }
+  }
+  if (tid == 0) opre[n] = base;
+  __syncthreads();
+  int32_t* uo = union_out + (size_t)i * cap;
+#pragma unroll
+  for (int e = 0; e < kUnRounds; ++e) {
+    const int x = e * kUnThreads + tid;
+    if (x < n) {
+      const int t = x / K, j = x - t * K;
+      int pos = -1;
+      if (j < mcount[t]) {
+        pos = 0;
+#pragma unroll
+        for (int q = 0; q < kMaxSelectQ; ++q)
+          if (q < qsel) pos += opre[q * K + lbs[e][q]] - opre[q * K];
+        if (own[e]) uo[pos] = lst[x];
+      }
+      upos_out[(size_t)i * n + x] = pos;
+    }
+  }
+  for (int x = base + tid; x < cap; x += kUnThreads) uo[x] = -1;
+}
+
+hs_status launch_topk_union(hs_pool* p, const int32_t* idx, int32_t n_req, int32_t qsel, int32_t k,
+                            int32_t* union_out, int32_t* upos_out, hipStream_t s) {
+  k_topk_union<<<n_req, kUnThreads, 0, s>>>(idx, qsel, k, p->d.top_k, union_out, upos_out);
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
 }

@@ -21,7 +21,7 @@ def make_pool(wl: W.Workload, device: str = "cuda", spare_pages: int = 0) -> Tie
                       max_requests=s.n_req, max_context=wl.max_context, kv_dtype=s.kv_dtype,
                       top_k=s.top_k, hot_rows=s.hot_rows, max_batch=s.n_req,
                       max_q_rows=s.q_per_req * s.heads, host_rows=int(wl.rows.shape[0]),
-                      device=device)
+                      select_q=s.q_per_req if s.select_k else 0, device=device)
 
 
 def store_bytes(wl: W.Workload) -> np.ndarray:
@@ -97,7 +97,16 @@ class StepBuffers:
         qdt = torch.float32 if s.q_dtype == "f32" else torch.bfloat16
         self.req_ids = torch.arange(R, dtype=torch.int32, device=dev)
         stride = -(-wl.max_context // 64) * 64  # 16-byte aligned rows
-        self.scores = torch.zeros(n_steps, R, stride, dtype=torch.float32, device=dev)
+        # speculative steps with a selection per query token: per-token
+        # scores, selections and union positions, and the union
+        self.union = s.select_k is not None
+        if self.union:
+            Q, k = s.q_per_req, s.select_k
+            self.scores = torch.zeros(n_steps, R, Q, stride, dtype=torch.float32, device=dev)
+            self.sel = torch.full((R, Q, k), -1, dtype=torch.int32, device=dev)
+            self.upos = torch.full((R, Q, k), -1, dtype=torch.int32, device=dev)
+        else:
+            self.scores = torch.zeros(n_steps, R, stride, dtype=torch.float32, device=dev)
         self.q = torch.zeros(n_steps, R, s.q_per_req, s.heads, W.ROW_DIM, dtype=qdt, device=dev)
         self.idx = torch.full((R, K), -1, dtype=torch.int32, device=dev)
         self.plan = torch.full((R, K), -1, dtype=torch.int32, device=dev)
@@ -107,7 +116,7 @@ class StepBuffers:
         self.sm_scale = float(wl.sm_scale)
 
     def upload(self, n: int, scores: np.ndarray, q: np.ndarray):
-        self.scores[n, :, :scores.shape[1]].copy_(torch.from_numpy(scores))
+        self.scores[n, ..., :scores.shape[-1]].copy_(torch.from_numpy(scores))
         if q.dtype == np.uint16:
             self.q[n].copy_(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16))
         else:
@@ -115,7 +124,14 @@ class StepBuffers:
 
 
 def decode_step(pool: TieredPool, buf: StepBuffers, n: int = 0):
-    """One step: top-K -> resolve -> sparse MLA attention (stream-ordered)."""
+    """One step: top-K -> resolve -> sparse MLA attention (stream-ordered).
+    A speculative step with a selection per query token selects per token,
+    resolves the union (buf.idx) once and attends per token through it."""
+    if buf.union:
+        pool.select_topk_union(buf.scores[n], buf.req_ids, buf.sel, buf.idx, buf.upos)
+        pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
+        pool.sparse_mla_decode_union(buf.q[n], buf.plan, buf.upos, buf.sm_scale, buf.out, buf.lse)
+        return
     pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
     pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
     pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)

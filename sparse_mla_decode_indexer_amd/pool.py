@@ -29,12 +29,12 @@ def _stream() -> int:
 class TieredPool:
     def __init__(self, *, page_size: int, num_pool_pages: int, max_requests: int, max_context: int,
                  kv_dtype: str, top_k: int, hot_rows: int = 0, max_batch: Optional[int] = None,
-                 max_q_rows: int = 128, host_rows: int, device: str = "cuda"):
+                 max_q_rows: int = 128, host_rows: int, select_q: int = 0, device: str = "cuda"):
         self.desc = B.HsPoolDesc(page_size=page_size, num_pool_pages=num_pool_pages,
                                  max_requests=max_requests, max_context=max_context, nope_dim=512,
                                  rope_dim=64, kv_dtype=B.DTYPE_CODES[kv_dtype], top_k=top_k,
                                  hot_rows=hot_rows, max_batch=max_batch or max_requests,
-                                 max_q_rows=max_q_rows, reserved0=0, host_rows=host_rows)
+                                 max_q_rows=max_q_rows, select_q=select_q, host_rows=host_rows)
         self.kv_dtype = kv_dtype
         self.sizes = B.pool_requirements(self.desc)
         self.device = torch.device(device)
@@ -105,6 +105,21 @@ class TieredPool:
     def select_topk(self, scores: torch.Tensor, req_ids: torch.Tensor, idx_out: torch.Tensor):
         B.select_topk(self.handle, scores.data_ptr(), scores.stride(0), req_ids.data_ptr(),
                       int(req_ids.numel()), idx_out.data_ptr(), _stream())
+
+    def select_topk_union(self, scores: torch.Tensor, req_ids: torch.Tensor, idx_out: torch.Tensor,
+                          union_out: torch.Tensor, upos_out: torch.Tensor):
+        """scores fp32 [n, Q, stride]; idx_out and upos_out int32 [n, Q, k]; union_out int32 [n, top_k]."""
+        n, Q, k = idx_out.shape
+        B.select_topk_union(self.handle, scores.data_ptr(), scores.stride(1), req_ids.data_ptr(), n, Q, k,
+                            idx_out.data_ptr(), union_out.data_ptr(), upos_out.data_ptr(), _stream())
+
+    def sparse_mla_decode_union(self, q: torch.Tensor, plan: torch.Tensor, upos: torch.Tensor, sm_scale: float,
+                                out: torch.Tensor, lse: Optional[torch.Tensor] = None):
+        """q [n, Q, H, 576]; plan [n, top_k] (of the union); upos [n, Q, k]."""
+        n_req, q_per_req, n_heads, _ = q.shape
+        qd = B.HS_F32 if q.dtype == torch.float32 else B.HS_BF16
+        B.sparse_mla_decode_union(self.handle, q.data_ptr(), qd, n_req, q_per_req, n_heads, plan.data_ptr(),
+                                  upos.data_ptr(), int(upos.shape[-1]), sm_scale, out.data_ptr(), _ptr(lse), _stream())
 
     def indexer_scores(self, iq: torch.Tensor, iw: torch.Tensor, ik: torch.Tensor, req_ids: torch.Tensor,
                        scores: torch.Tensor):

@@ -84,6 +84,13 @@ class WorkloadSpec:
     # table, hot buffer, scores and queries, and the slots of one request
     # share its context length.
     layers: int = 1
+    # Speculative steps with a selection per query token: each of the
+    # q_per_req query tokens selects select_k tokens (top_k is then the
+    # union capacity, >= q_per_req * select_k); query token 0 has the
+    # request's score chain, token t >= 1 that chain plus N(0, token_noise^2)
+    # drawn afresh every step.
+    select_k: Optional[int] = None
+    token_noise: float = 0.0
 
     @property
     def seed(self) -> int:
@@ -130,6 +137,14 @@ SPECS: Dict[str, WorkloadSpec] = {
         heads=128, q_per_req=4, top_k=2048, hot_rows=4096, steps=715,
         residency="budget", gpu_token_budget=9088, growth=(74160, 753, 220, 13),
         scores=("ar1", 0.9)),
+    # Speculative steps with one top-K per query token (1 + 3 drafts, 1,024
+    # tokens each) and one resolve of their union (capacity 4,096) per step;
+    # the agent shape with the aggregate GPU budget, so that misses occur.
+    "agent16-union": WorkloadSpec(
+        name="agent16-union", index=7, n_req=16, kv_dtype=KV_FP8, q_dtype="bf16",
+        heads=128, q_per_req=4, top_k=4096, hot_rows=4096, steps=715,
+        residency="budget", gpu_token_budget=9088, growth=(74160, 753, 220, 13),
+        scores=("ar1", 0.9), select_k=1024, token_noise=0.5),
 }
 
 
@@ -380,6 +395,11 @@ class ScoreStream:
                 out.append(n)
         return out
 
+    def next_tokens(self, lens: np.ndarray) -> np.ndarray:
+        """Per-query-token scores [R, Q, max_context] of the next
+        speculative step (token_scores of the next request scores)."""
+        return token_scores(self.wl, self.next(lens), lens, self.g)
+
     def next(self, lens: np.ndarray) -> np.ndarray:
         """Scores of the next step for context lengths `lens` [R]."""
         self.n += 1
@@ -411,6 +431,21 @@ class ScoreStream:
             self.state[r] = s
             out[r, :L] = s
         return out
+
+
+def token_scores(wl: Workload, base: np.ndarray, lens: np.ndarray, g: np.random.Generator) -> np.ndarray:
+    """Per-query-token scores [R, Q, max_context] of a speculative step from
+    the request scores `base` [R, max_context]: token 0 keeps them, token
+    t >= 1 adds N(0, token_noise^2) noise over each request's first lens[r]."""
+    s = wl.spec
+    R, Q = base.shape[0], s.q_per_req
+    out = np.repeat(base[:, None, :], Q, axis=1)
+    for r in range(R):
+        n = int(lens[r])
+        for t in range(1, Q):
+            out[r, t, :n] += (np.float32(s.token_noise) *
+                              g.standard_normal(n, dtype=np.float32)).astype(np.float32)
+    return out
 
 
 class QueryStream:

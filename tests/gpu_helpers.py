@@ -89,6 +89,13 @@ class ShardedOracle:
         res = list(self.pool.map(one, range(len(self.parts))))
         return {k: [x[k][0] for x in res] if res[0][k] else [] for k in res[0]}
 
+    def step_union(self, scores, q, lens, k_per_token, with_attention=True) -> Dict[str, List[np.ndarray]]:
+        def one(r):
+            return self.parts[r].step_union(scores[r:r + 1], None if q is None else q[r:r + 1], [lens[r]],
+                                            k_per_token, with_attention=with_attention)
+        res = list(self.pool.map(one, range(len(self.parts))))
+        return {k: [x[k][0] for x in res] if res[0][k] else [] for k in res[0]}
+
     def close(self):
         self.pool.shutdown(wait=True)
 
@@ -138,6 +145,8 @@ class Runner:
     def step(self, heads: Optional[Sequence[int]] = None, graph: bool = False):
         """Run one step on GPU and oracle and compare. `heads` restricts the
         attention comparison to those head indices (all query tokens)."""
+        if self.spec.select_k is not None:
+            return self._step_union(heads)
         s, wl = self.spec, self.wl
         lens = self.sched[self.n]
         if s.growth is not None:
@@ -200,6 +209,68 @@ class Runner:
             assert e <= ATTN_TOL, f"{tag} req {r}: attention rel err {e:.3e}"
             le = float(np.max(np.abs(l - l_ref) / np.maximum(1.0, np.abs(l_ref))))
             assert le <= LSE_TOL, f"{tag} req {r}: lse err {le:.3e}"
+        code = self.pool.device_error()
+        assert code[0] == 0, f"{tag}: device error {code}"
+        return ref
+
+    def _grow(self, lens):
+        s, wl = self.spec, self.wl
+        if s.growth is not None:
+            for r in range(s.n_req):
+                if self.incremental:
+                    ps = s.page_size
+                    a_, b_ = -(-int(self.cur_len[r]) // ps), -(-int(lens[r]) // ps)
+                    Hn.set_request(self.pool, wl, r, int(lens[r]), first_page=a_, num_pages=b_ - a_)
+                else:
+                    Hn.set_request(self.pool, wl, r, int(lens[r]))
+        self.cur_len = np.asarray(lens).copy()
+
+    def _step_union(self, heads):
+        """A speculative step with a selection per query token: per-token
+        top-K, union and union positions, one resolve of the union, and
+        per-token attention over its own rows, against DecodeOracle.step_union."""
+        s, wl = self.spec, self.wl
+        lens = self.sched[self.n]
+        self._grow(lens)
+        sc = self.scores.next_tokens(lens)
+        q = self.queries.next()
+        self.buf.upload(0, sc, q)
+        Hn.decode_step(self.pool, self.buf)
+        torch.cuda.synchronize()
+        ref = self.oracle.step_union(sc, None, lens, s.select_k, with_attention=False)
+        self.n += 1
+        tag = f"{s.name} step {self.n}"
+        sel = self.buf.sel.cpu().numpy()
+        uni = self.buf.idx.cpu().numpy()
+        upos = self.buf.upos.cpu().numpy()
+        plan = self.buf.plan.cpu().numpy()
+        counts = self.buf.counts.cpu().numpy()
+        for r in range(s.n_req):
+            assert np.array_equal(sel[r], ref["sel"][r]), f"{tag} req {r}: per-token top-K differs"
+            assert np.array_equal(uni[r], ref["union"][r]), f"{tag} req {r}: union differs"
+            assert np.array_equal(upos[r], ref["upos"][r]), f"{tag} req {r}: union positions differ"
+            assert np.array_equal(counts[r], ref["counts"][r]), f"{tag} req {r}: counts {counts[r]} vs {ref['counts'][r]}"
+            assert np.array_equal(plan[r], ref["plan"][r]), f"{tag} req {r}: plan differs"
+            assert counts[r].sum() == int((ref["union"][r] >= 0).sum())
+        if self.check_state:
+            self._check_state(tag)
+        self._check_rows(uni, plan, tag)
+        out = self.buf.out.cpu().numpy()
+        lse = self.buf.lse.cpu().numpy()
+        hs = list(range(s.heads)) if heads is None else list(heads)
+        qd = q_f64(q[:, :, hs])
+        for r in range(s.n_req):
+            for t in range(s.q_per_req):
+                toks = ref["sel"][r][t][ref["sel"][r][t] >= 0]
+                rows = self.oracle.logical_rows(r, toks)
+                o_ref, l_ref = mla_attention(qd[r][t], rows, float(wl.sm_scale))
+                o, l = out[r][t][hs], lse[r][t][hs]
+                e = attn_rel_err(o, o_ref)
+                self.max_err = max(self.max_err, e)
+                self.max_elem_err = max(self.max_elem_err, attn_elem_err(o, o_ref))
+                assert e <= ATTN_TOL, f"{tag} req {r} token {t}: attention rel err {e:.3e}"
+                le = float(np.max(np.abs(l - l_ref) / np.maximum(1.0, np.abs(l_ref))))
+                assert le <= LSE_TOL, f"{tag} req {r} token {t}: lse err {le:.3e}"
         code = self.pool.device_error()
         assert code[0] == 0, f"{tag}: device error {code}"
         return ref

@@ -17,7 +17,7 @@ def _lib():
 def test_exports_every_declared_function():
     L = _lib()
     names = B.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert set(B._SIGS) == set(names)
@@ -26,7 +26,7 @@ def test_exports_every_declared_function():
 def desc(**kw):
     d = dict(page_size=64, num_pool_pages=128, max_requests=2, max_context=8192, nope_dim=512,
              rope_dim=64, kv_dtype=B.HS_BF16, top_k=2048, hot_rows=0, max_batch=2, max_q_rows=128,
-             reserved0=0, host_rows=16384)
+             select_q=0, host_rows=16384)
     d.update(kw)
     return B.HsPoolDesc(**d)
 
@@ -51,7 +51,8 @@ def test_requirements_sizes():
     (dict(kv_dtype=7), 3),
     (dict(top_k=0), 1),
     (dict(max_batch=3), 1),
-    (dict(reserved0=1), 1),
+    (dict(select_q=9), 1),
+    (dict(select_q=-1), 1),
 ])
 def test_requirements_rejects(kw, status):
     _lib()
