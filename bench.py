@@ -156,7 +156,8 @@ def main():
     ss, qs = W.ScoreStream(wl), W.QueryStream(wl)
     host_scores, host_q = [], []
     for n in range(T):
-        sc, q = ss.next(sched[n]), qs.next()
+        sc = ss.next_tokens(sched[n]) if spec.select_k else ss.next(sched[n])
+        q = qs.next()
         buf.upload(n, sc, q)
         if n < 64 and sc.nbytes * (n + 1) < (1 << 30):
             host_scores.append(sc)
@@ -215,16 +216,25 @@ def main():
     R, Kt, S = spec.n_req, spec.top_k, spec.hot_rows
     rb = W.row_bytes(spec.kv_dtype) + (4 if spec.kv_dtype == "fp8" else 0)
     lens = np.asarray(wl.ctx0, dtype=np.int64)
-    rows_per_step = int(np.minimum(Kt, lens).sum())
     misses_per_step = dc[2] / K
     qb = 4 if spec.q_dtype == "f32" else 2
     QH = spec.q_per_req * spec.heads
     # algorithmic bytes of one step (what the method must move)
-    b_topk = 4 * lens.sum() + 4 * R * Kt
-    b_resolve_hbm = R * (12 * Kt + 8 * S) + misses_per_step * rb
+    if spec.select_k:  # a top-K per query token, one resolve of the union
+        Qn, kt = spec.q_per_req, spec.select_k
+        rows_per_step = int(dc.sum() / K)  # union rows resolved per step
+        b_topk = 4 * Qn * lens.sum() + 4 * R * Qn * kt + 8 * R * Qn * kt + 4 * R * Kt
+        b_resolve_hbm = R * 8 * S + 12 * rows_per_step + misses_per_step * rb
+        attn_rows = Qn * int(np.minimum(kt, lens).sum())  # each token reads its own rows
+        b_attn = attn_rows * rb + R * QH * (576 * qb + 512 * 4 + 4) + 8 * R * Qn * kt
+        flops_attn = 2.0 * spec.heads * attn_rows * (576 + 512)
+    else:
+        rows_per_step = int(np.minimum(Kt, lens).sum())
+        b_topk = 4 * lens.sum() + 4 * R * Kt
+        b_resolve_hbm = R * (12 * Kt + 8 * S) + misses_per_step * rb
+        b_attn = rows_per_step * rb + R * QH * (576 * qb + 512 * 4 + 4) + 4 * R * Kt
+        flops_attn = 2.0 * QH * rows_per_step * (576 + 512)
     b_pcie = misses_per_step * rb
-    b_attn = rows_per_step * rb + R * QH * (576 * qb + 512 * 4 + 4) + 4 * R * Kt
-    flops_attn = 2.0 * QH * rows_per_step * (576 + 512)
 
     roof = None
     if not args.no_roofline:
@@ -237,12 +247,9 @@ def main():
         torch.cuda._sleep(int(2e8))  # let the host queue run ahead of the GPU
         for j, n in enumerate(range(Wm, T)):
             ev = evs[j]
-            ev[0].record(stream)
-            pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
-            ev[1].record(stream)
-            pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
-            ev[2].record(stream)
-            pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)
+            for a, call in enumerate(entry_calls(pool, buf, n)):
+                ev[a].record(stream)
+                call()
             ev[3].record(stream)
         torch.cuda.synchronize()
         dur = np.array([[ev[a].elapsed_time(ev[a + 1]) for a in range(3)] for ev in evs])  # ms
@@ -348,7 +355,9 @@ def main():
                             if group > 0 else "three entry points in sequence on one stream"),
                    **({"growth": "context frozen at the first step's length"}
                       if spec.growth is not None else {}),
-                   **({"layers": spec.layers} if spec.layers > 1 else {})},
+                   **({"layers": spec.layers} if spec.layers > 1 else {}),
+                   **({"top_k_per_query_token": spec.select_k, "union_capacity": spec.top_k}
+                      if spec.select_k else {})},
         **({"layer_steps_per_s": round(value * spec.layers, 1)} if spec.layers > 1 else {}),
         "rows_resolved_per_s": round(rows_per_step * value, 1),
         "misses_per_step": round(float(misses_per_step), 1),
@@ -373,7 +382,7 @@ def main():
 
 # HIP kernels behind each entry point (name prefixes as the profiler lists them)
 ENTRY_KERNELS = {
-    "select_topk": ["k_topk_filter", "k_topk_select"],
+    "select_topk": ["k_topk_filter", "k_topk_select", "k_topk_union"],
     "resolve_rows": ["k_resolve"],
     "sparse_mla_decode": ["k_attn_mfma", "k_attn_combine"],
 }
@@ -417,6 +426,19 @@ def measured_traffic(workload: str, kernels):
     return total or None
 
 
+def entry_calls(pool, buf, n):
+    """The step's three entry points as calls for step n (top-K, resolve,
+    attention; the union forms for a speculative step with a selection per
+    query token)."""
+    if buf.union:
+        return [lambda: pool.select_topk_union(buf.scores[n], buf.req_ids, buf.sel, buf.idx, buf.upos),
+                lambda: pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts),
+                lambda: pool.sparse_mla_decode_union(buf.q[n], buf.plan, buf.upos, buf.sm_scale, buf.out, buf.lse)]
+    return [lambda: pool.select_topk(buf.scores[n], buf.req_ids, buf.idx),
+            lambda: pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts),
+            lambda: pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)]
+
+
 def timed_entry_points(pool, buf, steps):
     """Run the given steps eagerly with HIP events around each entry point
     (a spin kernel first lets the host queue run ahead). Returns the average
@@ -428,12 +450,9 @@ def timed_entry_points(pool, buf, steps):
     torch.cuda._sleep(int(2e8))
     for j, n in enumerate(steps):
         ev = evs[j]
-        ev[0].record(stream)
-        pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
-        ev[1].record(stream)
-        pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
-        ev[2].record(stream)
-        pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)
+        for a, call in enumerate(entry_calls(pool, buf, n)):
+            ev[a].record(stream)
+            call()
         ev[3].record(stream)
     torch.cuda.synchronize()
     dur = np.array([[ev[a].elapsed_time(ev[a + 1]) for a in range(3)] for ev in evs]) * 1e3
@@ -546,7 +565,10 @@ def cpu_baseline(wl, host_scores, host_q, sched, budget_s):
         j = n % m
         q = host_q[j]
         qd = bf16_decode(q) if q.dtype == np.uint16 else q.astype(np.float64)
-        orc.step(host_scores[j], qd, sched[j], with_attention=True)
+        if s.select_k:
+            orc.step_union(host_scores[j], qd, sched[j], s.select_k, with_attention=True)
+        else:
+            orc.step(host_scores[j], qd, sched[j], with_attention=True)
         n += 1
     el = time.perf_counter() - t0
     try:  # the BLAS threads numpy actually runs with
