@@ -95,7 +95,7 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   of.rs_mdst = take(8 * B * (size_t)K);
   of.rs_mslot = take(4 * B * (size_t)K);
   of.rs_mold = take(4 * B * (size_t)K);
-  of.rs_ticket = take(16);
+  of.rs_ticket = take(16 * B);  // per batch position: ticket, sequence, done
   of.ru_list = take(8 * B * (size_t)kRuMaxList);
   of.ru_ncopy = take(4 * B);
   of.at_part_rows = (int64_t)B * d->max_q_rows * kAttSplitCap;

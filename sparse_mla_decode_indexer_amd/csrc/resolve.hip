@@ -4,15 +4,16 @@
 // LRU entry, or on a miss copies the single row from pinned host memory into
 // the LRU slot; [P3] §"融合内核与CUDA图兼容": the pass is graph-capturable).
 //
-// One kernel, two kinds of workgroup, roles handed out by a device ticket
-// counter in the order workgroups start:
-//   bookkeeper (tickets 0 .. n_req-1), one per request: classifies the K
+// One kernel, two kinds of workgroup. Workgroup b serves batch position
+// i = b mod n_req; the workgroups of one position take roles from that
+// position's ticket counter in the order they start:
+//   bookkeeper (ticket 0), one per request: classifies the K
 //     tokens (resident > hot > miss), stamps the hit slots, picks the victims
 //     and rewrites the LRU order with ordered compactions in LDS, writes the
 //     plan and the counts, and for every plan position the hot slot and that
 //     slot's old token (misses) and last the copy destination: the pool row
 //     a miss is copied to, or -1, tagged with the launch's epoch;
-//   copy workgroup (request i, part c), one per 64 plan positions (4 per
+//   copy workgroup (ticket 1 + c: part c), one per 64 plan positions (4 per
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
 //     store over PCIe right away; each wave then waits until its four copy
@@ -31,11 +32,14 @@
 // A copy workgroup holds a later ticket than its bookkeeper, which is
 // therefore running and never waits, so the wait always ends; it is also
 // bounded (HS_DEV_TIMEOUT is raised past the bound and the copy skipped).
-// Epochs. Every workgroup reads the launch sequence number before it takes
-// its ticket, and counts itself done at its end; the last workgroup to be
-// done advances the sequence and clears the ticket and done counters, so all
-// workgroups of one launch share one epoch, the next launch has another and
-// starts from cleared counters, and nothing waits for the end of a launch.
+// Epochs. Every workgroup reads its position's launch sequence number
+// before it takes its ticket, and counts itself done at its end; the last
+// workgroup of the position to be done advances the sequence and clears the
+// position's ticket and done counters, so all workgroups of one launch and
+// position share one epoch, the next launch has another and starts from
+// cleared counters, and nothing waits for the end of a launch. The counters
+// are per batch position, so no atomic is contended by more than one
+// request's workgroups.
 // A destination entry is a 64-bit (epoch, pool row) pair, and a copy wave
 // takes an entry as published only when it carries its own launch's epoch.
 // An entry left from an earlier launch therefore never passes for this
@@ -64,7 +68,7 @@ struct RsScratch {
   uint64_t* mdst;                 // [batch][K] (epoch << 32) | pool row a missed position is copied to, else -1
   int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
   int32_t* mold;                  // [batch][K] token that slot held before (or -1)
-  uint32_t* ticket;               // [0]: roles handed out; [1]: launch sequence (epoch - 1); [2]: workgroups done
+  uint32_t* ctl;                  // [batch][4]: roles handed out, launch sequence (epoch - 1), workgroups done
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
 
@@ -600,37 +604,37 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   __shared__ RsStatic st;
   extern __shared__ __align__(16) unsigned char rs_dyn[];
   const int tid = threadIdx.x;
+  const int i = (int)(blockIdx.x % (unsigned)a.n_req);  // batch position served
+  uint32_t* ctl = sc.ctl + 4 * (size_t)i;
   if (tid == 0) {
-    const uint32_t seq = __hip_atomic_load(&sc.ticket[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t seq = __hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the ticket is taken only after the sequence load has returned, so the
     // sequence cannot advance before this workgroup has read it
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     st.epoch = seq + 1u;
-    st.role = (int)atomicAdd(&sc.ticket[0], 1u);
+    st.role = (int)atomicAdd(&ctl[0], 1u);
   }
   __syncthreads();
   const int role = st.role;
-  if (role < a.n_req) {
-    bookkeep(a, v, sc, st, rs_dyn, role);
+  if (role == 0) {
+    bookkeep(a, v, sc, st, rs_dyn, i);
   } else {
-    const int q = role - a.n_req;
-    const int i = q / sc.parts;
-    copy_part<ROW_BYTES, FP8>(a, v, sc, i, q - i * sc.parts, st.epoch);
+    copy_part<ROW_BYTES, FP8>(a, v, sc, i, role - 1, st.epoch);
   }
-  // The last workgroup of the launch to finish (every other one has taken
-  // its ticket and read the sequence by then) prepares the next launch.
+  // The last workgroup of this position to finish (every other one has
+  // taken its ticket and read the sequence by then) prepares the next launch.
   __syncthreads();
   if (tid == 0) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
-    if (atomicAdd(&sc.ticket[2], 1u) == gridDim.x - 1) {
+    if (atomicAdd(&ctl[2], 1u) == (uint32_t)sc.parts) {
       const uint32_t next = st.epoch == kRsSeqWrap ? 0u : st.epoch;  // sequence + 1, wrapped
-      __hip_atomic_store(&sc.ticket[1], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&sc.ticket[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&sc.ticket[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctl[1], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ctl[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -648,7 +652,7 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   sc.mdst = reinterpret_cast<uint64_t*>(p->state + p->off.rs_mdst);
   sc.mslot = reinterpret_cast<int32_t*>(p->state + p->off.rs_mslot);
   sc.mold = reinterpret_cast<int32_t*>(p->state + p->off.rs_mold);
-  sc.ticket = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);
+  sc.ctl = reinterpret_cast<uint32_t*>(p->state + p->off.rs_ticket);
   sc.parts = (p->d.top_k + kRsPart - 1) / kRsPart;
   RsArgs a{idx, req_ids, n_req,
            pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
