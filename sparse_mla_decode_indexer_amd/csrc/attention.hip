@@ -27,9 +27,15 @@
 //     waves of a q block then hold the full scores;
 //   - the scores land with each lane holding 8 rows of one query, exactly
 //     the B operand of P^T: p stays in registers, split as hi + lo bf16
-//     terms (~16 significant bits per weight; a single bf16 term would cost
-//     up to 2^-8 relative error per weight); fp8 rows fold their scale into
-//     the logit and into p in fp32;
+//     terms for bf16 rows (~16 significant bits per weight; a single bf16
+//     term would cost up to 2^-8 relative error per weight); fp8 rows fold
+//     their scale into the logit and into p in fp32;
+//   - fp8 rows run both contractions in fp16 (codes widen to fp16 exactly;
+//     each query half is scaled by a power of two so that its largest
+//     magnitude lies in [2^14, 2^15), and the partial scores are scaled
+//     back exactly), so p enters as a single fp16 term (11 significant
+//     bits, round to nearest even) of p * row scale / the split's largest
+//     row scale: 16 PV MFMAs per tile instead of 32;
 //   - PV: O^T (256 dims x 16 q) += V^T . P^T; V^T operands come from 8x8
 //     register transposes of row-major LDS reads, in the same row order as
 //     P^T;
@@ -103,6 +109,19 @@ __device__ inline f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline f32x4_t mfma16h(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+
+// Two floats -> one dword of two fp16, round to nearest even.
+__device__ inline uint32_t pack_f16(float a, float b) {
+  const f16x2_t h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // s_waitcnt immediate: vmcnt(n) (6 bits, split over bits 3:0 and 15:14),
 // expcnt and lgkmcnt left at their maximum (no wait).
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 0xF) | ((n & 0x30) << 10); }
@@ -121,6 +140,14 @@ __device__ inline void fp8x4_to_bf16(uint32_t w, uint32_t* o) {
   const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
   o[0] = pack_hi(f01[0], f01[1]);
   o[1] = pack_hi(f23[0], f23[1]);
+}
+
+// 4 OCP e4m3 codes -> 4 fp16 (exact: every e4m3 value is an fp16 value).
+__device__ inline void fp8x4_to_f16(uint32_t w, uint32_t* o) {
+  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  o[0] = pack_f16(f01[0], f01[1]);
+  o[1] = pack_f16(f23[0], f23[1]);
 }
 
 // Workgroup barrier for LDS exchanges that leaves the tile prefetch in
@@ -199,6 +226,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
   __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
   __shared__ f32x4_t sbuf[2][QB][2][64];  // partial scores [key half][q block][row block][lane]
+  __shared__ float smax_s[2 * QB];        // fp8: largest row scale seen by each wave
   constexpr int kAttThreads = 128 * QB;
   constexpr int kQPerWG = 16 * QB;
 
@@ -229,6 +257,13 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     prow_s[j] = pr;
     if (FP8) scale_s[j] = pr >= 0 ? pool_scales[pr] : 0.f;
   }
+  if constexpr (FP8) {  // the split's largest row scale (the fp16 weights are relative to it)
+    float mx = 0.f;
+    for (int j = tid; j < nt * kTile; j += kAttThreads) mx = fmaxf(mx, scale_s[j]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) smax_s[wave] = mx;
+  }
   // Q^T operand for key dims 288*half .. +288: lane holds query row qh,
   // dims 288*half + 32*kk + 8*kg .. +8. Lanes past the last query row
   // compute on row 0 and write nothing. The registers are first read by the
@@ -241,6 +276,17 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     for (int kk = 0; kk < kKSteps; ++kk) qop[kk] = *reinterpret_cast<const u32x4_t*>(qr + 32 * kk + 8 * kg);
   }
   lds_sync();
+  float sref = 1.f, inv_sref = 1.f;  // fp8: weights are p * scale / sref
+  if constexpr (FP8) {
+    float mx = 0.f;
+#pragma unroll
+    for (int w = 0; w < 2 * QB; ++w) mx = fmaxf(mx, smax_s[w]);
+    if (mx > 0.f) {
+      sref = mx;
+      inv_sref = 1.f / mx;
+    }
+  }
+  int q_shift = 0;  // fp8: this wave's query half was scaled by 2^q_shift
 
   // Gather of a tile into LDS (wave-contiguous LDS targets). This thread's
   // chunk positions p = k * threads + tid are the same in every tile; their
@@ -326,10 +372,10 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
         const int r = x / kRawChunks, c = x - r * kRawChunks;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cur + x * 16);
         uint32_t w[8];
-        fp8x4_to_bf16(v[0], w);
-        fp8x4_to_bf16(v[1], w + 2);
-        fp8x4_to_bf16(v[2], w + 4);
-        fp8x4_to_bf16(v[3], w + 6);
+        fp8x4_to_f16(v[0], w);
+        fp8x4_to_f16(v[1], w + 2);
+        fp8x4_to_f16(v[2], w + 4);
+        fp8x4_to_f16(v[3], w + 6);
         *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
         *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c + 1) * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
       }
@@ -347,13 +393,20 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma16(ka[kk][rb], qop[kk], sacc[rb]);
+      for (int rb = 0; rb < 2; ++rb)
+        sacc[rb] = FP8 ? mfma16h(ka[kk][rb], qop[kk], sacc[rb]) : mfma16(ka[kk][rb], qop[kk], sacc[rb]);
     // loads kQkAhead key steps ahead of their MFMAs
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kQkAhead, 0);
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
       if (kk + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    if constexpr (FP8) {  // undo the query half's power-of-two scale (exact)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sacc[rb][v] = ldexpf(sacc[rb][v], -q_shift);
     }
     sbuf[half][qb][0][lane] = sacc[0];
     sbuf[half][qb][1][lane] = sacc[1];
@@ -381,21 +434,25 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : (grow ? 0.f : 1.f);
     m_run = m_new;
-    u32x4_t bhi, blo;  // P^T operand (hi and lo parts), rows krow(kg, 0..7)
+    u32x4_t bhi, blo;  // P^T operand (hi and lo parts; fp8: one fp16 term), rows krow(kg, 0..7)
     {
       float psum = 0.f, a[8], lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(s[e] - m_use);
         psum += pe;
-        a[e] = FP8 ? pe * rs[e] : pe;
+        a[e] = FP8 ? pe * (rs[e] * inv_sref) : pe;
         lo[e] = a[e] - __uint_as_float(__float_as_uint(a[e]) & 0xFFFF0000u);
       }
       lpart = lpart * alpha + psum;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        bhi[d] = pack_hi(a[2 * d], a[2 * d + 1]);
-        blo[d] = pack_hi(lo[2 * d], lo[2 * d + 1]);
+        if constexpr (FP8) {
+          bhi[d] = pack_f16(a[2 * d], a[2 * d + 1]);
+        } else {
+          bhi[d] = pack_hi(a[2 * d], a[2 * d + 1]);
+          blo[d] = pack_hi(lo[2 * d], lo[2 * d + 1]);
+        }
       }
     }
 
@@ -413,15 +470,20 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     }
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
-      acc[b] = mfma16(va[b], bhi, acc[b]);
-      acc[b] = mfma16(va[b], blo, acc[b]);
+      if constexpr (FP8) {
+        acc[b] = mfma16h(va[b], bhi, acc[b]);
+      } else {
+        acc[b] = mfma16(va[b], bhi, acc[b]);
+        acc[b] = mfma16(va[b], blo, acc[b]);
+      }
     }
     // Instruction order: the operand loads run kPvAhead blocks ahead of
     // their MFMAs, so LDS latency overlaps the MFMAs of earlier blocks.
+    constexpr int kPvMfma = FP8 ? 1 : 2;  // MFMAs per value block
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvMfma, 0);
       if (b + kPvAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   };
@@ -435,6 +497,28 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     rows_of(2, rows_next);
   }
   __builtin_amdgcn_s_waitcnt(kWaitTwo);  // the query loads (issued before the gathers)
+  if constexpr (FP8) {
+    // Query half -> fp16, scaled by the power of two 2^q_shift that puts its
+    // largest magnitude in [2^14, 2^15): exact for every element within 2^24
+    // of that largest one (smaller ones contribute below 2^-24 of it).
+    float m = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        m = fmaxf(m, fabsf(__uint_as_float(qop[kk][d] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(qop[kk][d] & 0xFFFF0000u)));
+      }
+    m = max_across_kg(m);
+    const int ex = (int)((__float_as_uint(m) >> 23) & 0xFF);
+    q_shift = m > 0.f ? 141 - (ex == 0 ? 1 : ex) : 0;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        qop[kk][d] = pack_f16(ldexpf(__uint_as_float(qop[kk][d] << 16), q_shift),
+                              ldexpf(__uint_as_float(qop[kk][d] & 0xFFFF0000u), q_shift));
+  }
   // Full turns of the ring, then the 0-2 remaining tiles: every path issues
   // the same number of gathers per tile, so the compiler's count of pending
   // loads matches the waits above at every tile.
@@ -455,7 +539,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // softmax denominator: sum over the 4 lanes (row groups) of each query
   const float l = sum_across_kg(lpart);
   if (!qvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l > 0.f ? sref / l : 0.f;  // (sref = 1 for bf16 rows)
   const float lse2 = l > 0.f ? m_run + __log2f(l) : -INFINITY;
   float* dst;
   if (n_splits == 1) {
