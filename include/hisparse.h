@@ -298,7 +298,15 @@ hs_status hs_indexer_scores(hs_pool* pool, const void* iq, const float* iw, cons
  *   - counts_out[i] (device int32 [n_req][3], may be NULL) = resident, hot,
  *     miss counts; they sum to min(top_k, L_r).
  * Each request's step counter advances by one. A request must appear at most
- * once per call. Errors: INVALID_ARGUMENT, CAPACITY. */
+ * once per call. Errors: INVALID_ARGUMENT, CAPACITY.
+ * A copy workgroup waits for its request's plan with a bounded number of
+ * polls (2^20, at least 0.1 s; the environment variable
+ * HS_RESOLVE_SPIN_LIMIT, read at each call, overrides it for tests). A wait
+ * that gives up raises HS_DEV_TIMEOUT and copies nothing for its positions:
+ * that call's plan and the hot buffers of its requests are then unusable;
+ * after hs_clear_device_error and HS_RESET_HOT on those requests the next
+ * call is exact (a destination published late by the call that gave up
+ * carries that call's epoch and is never taken by a later call). */
 hs_status hs_resolve_rows(hs_pool* pool, const int32_t* idx, const int32_t* req_ids,
                           int32_t n_req, int32_t* plan_out, int32_t* counts_out,
                           hipStream_t stream);

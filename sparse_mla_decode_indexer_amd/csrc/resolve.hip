@@ -56,6 +56,8 @@
 // by sorting the untouched slots by (stamp, slot).
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include "hs_internal.h"
 
 namespace hs {
@@ -92,6 +94,7 @@ struct RsArgs {
   int n_req;
   int P, Q;    // plan and LRU positions per bookkeeper thread
   int pt_lds;  // page-table entries staged in LDS (0: look up in global memory)
+  int spin_limit;  // polls of a destination before a copy wave gives up
   int32_t* plan_out;
   int32_t* counts_out;
   const uint8_t* host_rows;
@@ -548,10 +551,10 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
       md = (int32_t)(uint32_t)w;
     }
     if (!__any(pending)) break;  // (loop condition uniform per wave)
-    if (++spins > kSpinLimit) break;
+    if (++spins > a.spin_limit) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if (spins > kSpinLimit) {  // nothing of this wave's positions is written
+  if (spins > a.spin_limit) {  // nothing of this wave's positions is written
     if (lane == 0) raise_error(v.error, HS_DEV_TIMEOUT, (uint32_t)i, (uint32_t)j0);
     return;
   }
@@ -639,6 +642,15 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   }
 }
 
+// Polls before a copy wave gives up: kSpinLimit, or HS_RESOLVE_SPIN_LIMIT
+// when set (read at each call; a test hook that makes the wait give up).
+static int spin_limit() {
+  const char* s = getenv("HS_RESOLVE_SPIN_LIMIT");
+  if (!s) return kSpinLimit;
+  const int v = atoi(s);
+  return v >= 0 ? v : kSpinLimit;
+}
+
 static int pow2_at_least(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -657,7 +669,7 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
   RsArgs a{idx, req_ids, n_req,
            pow2_at_least((p->d.top_k + kRsThreads - 1) / kRsThreads),
            max(4, pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads)),
-           v.pages_per_req <= kRsPtLds ? v.pages_per_req : 0,
+           v.pages_per_req <= kRsPtLds ? v.pages_per_req : 0, spin_limit(),
            plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
            p->host_scales, p->pool_rows, p->pool_scales};
   const size_t dyn =

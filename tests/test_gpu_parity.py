@@ -10,6 +10,7 @@ import torch
 
 from gpu_helpers import Runner, log, small
 from oracle import mla_attention, select_topk
+from sparse_mla_decode_indexer_amd import harness as Hn
 from sparse_mla_decode_indexer_amd import workload as W
 from sparse_mla_decode_indexer_amd.pool import TieredPool
 
@@ -630,6 +631,44 @@ def test_pipelined_step_over_request_groups(group):
     rn = Runner(wl, group=group)
     try:
         for _ in range(4):
+            rn.step(heads=[0, 77])
+    finally:
+        rn.close()
+
+
+def test_resolve_wait_that_gives_up_then_hot_reset_is_exact(monkeypatch):
+    """A copy wave whose bounded wait gives up raises HS_DEV_TIMEOUT (batch
+    and plan position in range) instead of hanging; after clearing the error
+    and resetting the hot buffers (the documented recovery) the following
+    steps are bit-exact with the oracle, so no destination published late by
+    the call that gave up is taken by a later call (each carries its call's
+    epoch). The wait is made to give up with HS_RESOLVE_SPIN_LIMIT=0 (one
+    poll); whether it does depends on timing, and both outcomes are checked."""
+    spec = small("batch32", n_req=8, ctx_range=(8192, 40000), steps=5)
+    log("[gpu] resolve wait giving up (spin limit 0), then hot reset")
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        rn.step()
+        monkeypatch.setenv("HS_RESOLVE_SPIN_LIMIT", "0")
+        lens = rn.sched[rn.n]
+        sc, q = rn.scores.next(lens), rn.queries.next()
+        rn.buf.upload(0, sc, q)
+        Hn.decode_step(rn.pool, rn.buf)
+        torch.cuda.synchronize()
+        rn.oracle.step(sc, None, lens, with_attention=False)
+        rn.n += 1
+        monkeypatch.delenv("HS_RESOLVE_SPIN_LIMIT")
+        code = rn.pool.device_error()
+        assert code[0] in (0, 5), code
+        if code[0] == 5:
+            assert code[1] < spec.n_req and code[2] < spec.top_k and code[2] % 4 == 0, code
+        log(f"[gpu]   device error after the spin-limited call: {code}")
+        rn.pool.clear_device_error()
+        for r in range(spec.n_req):
+            Hn.set_request(rn.pool, wl, r, int(lens[r]), reset_hot=True)
+            rn.oracle.hot[r].reset()
+        for _ in range(3):
             rn.step(heads=[0, 77])
     finally:
         rn.close()
