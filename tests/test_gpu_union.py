@@ -99,3 +99,62 @@ def test_union_full_size_first_turns():
                     f"{np.asarray(ref['counts']).sum(axis=0).tolist()}, max err {rn.max_err:.2e}")
     finally:
         rn.close()
+
+
+def _graph_vs_eager(spec, step_fn, replays=4):
+    """Capture one step in a hipGraph on pool B and replay it `replays`
+    times, with new inputs copied in eagerly between the replays; the same
+    steps run eagerly on twin pool A. Every replay's outputs and the final
+    LRU state must be bit-identical to the eager run."""
+    from sparse_mla_decode_indexer_amd import harness as Hn
+    wl_a, wl_b = W.generate(spec), W.generate(spec)
+    pa, pb = Hn.make_pool(wl_a), Hn.make_pool(wl_b)
+    try:
+        Hn.load_workload(pa, wl_a)
+        Hn.load_workload(pb, wl_b)
+        ba, bb = Hn.StepBuffers(wl_a), Hn.StepBuffers(wl_b)
+        ss, qs = W.ScoreStream(wl_a), W.QueryStream(wl_a)
+        nxt = (lambda: ss.next_tokens(wl_a.ctx0)) if spec.select_k else (lambda: ss.next(wl_a.ctx0))
+        sc, q = nxt(), qs.next()
+        ba.upload(0, sc, q)
+        bb.upload(0, sc, q)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_fn(pb, bb)
+        for n in range(replays):
+            if n > 0:
+                sc, q = nxt(), qs.next()
+                ba.upload(0, sc, q)
+                bb.upload(0, sc, q)
+            torch.cuda.synchronize()
+            g.replay()
+            step_fn(pa, ba)
+            torch.cuda.synchronize()
+            for name in ("idx", "plan", "counts", "out", "lse") + (("sel", "upos") if spec.select_k else ()):
+                assert torch.equal(getattr(ba, name), getattr(bb, name)), f"replay {n}: {name}"
+        sa, sb = pa.state_views(), pb.state_views()
+        for k in ("slot_tag", "slot_stamp", "lru_order", "rev", "step", "page_stamp"):
+            assert torch.equal(sa[k], sb[k]), k
+        assert pa.device_error()[0] == 0 and pb.device_error()[0] == 0
+    finally:
+        pa.close()
+        pb.close()
+
+
+def test_union_step_graph_replays_match_eager():
+    log("[gpu] union step: hipGraph replays vs eager")
+    from sparse_mla_decode_indexer_amd import harness as Hn
+    _graph_vs_eager(_union_spec(steps=4), lambda pool, buf: Hn.decode_step(pool, buf, 0))
+
+
+def test_noalloc_attention_graph_replays_match_eager():
+    """The allocation-free attention entry point (the form for callers under
+    graph capture) inside a captured step, replayed with new inputs."""
+    log("[gpu] no-alloc attention step: hipGraph replays vs eager")
+
+    def step(pool, buf):
+        pool.select_topk(buf.scores[0], buf.req_ids, buf.idx)
+        pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
+        pool.sparse_mla_decode_noalloc(buf.q[0], buf.plan, buf.sm_scale, buf.out, buf.lse)
+    _graph_vs_eager(small("batch32", n_req=3, ctx_range=(8192, 30000), steps=4), step)
