@@ -390,7 +390,7 @@ ENTRY_KERNELS = {
 
 # Sources the decode-step kernels (top-K, resolve, attention) are built from:
 # the counters recorded for them stay valid while these files are unchanged.
-STEP_SOURCES = ["sparse_mla_decode_indexer_amd/csrc/topk.hip", "sparse_mla_decode_indexer_amd/csrc/resolve.hip",
+STEP_SOURCES = ["sparse_mla_decode_indexer_amd/csrc/topk.hip", "sparse_mla_decode_indexer_amd/csrc/topk_select.h", "sparse_mla_decode_indexer_amd/csrc/resolve.hip",
                 "sparse_mla_decode_indexer_amd/csrc/attention.hip", "sparse_mla_decode_indexer_amd/csrc/hs_internal.h",
                 "include/hisparse.h"]
 
