@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--group", type=int, default=-1,
                     help="requests per group of the pipelined step (harness.PipelinedStep); -1, the "
                          "default: the three entry points in sequence on one stream")
+    ap.add_argument("--fused", action="store_true",
+                    help="top-K and resolve as one call (hs_select_resolve) in the timed step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
@@ -146,13 +148,14 @@ def main():
     Hn.load_workload(pool, wl)
     buf = Hn.StepBuffers(wl, device=dev, n_steps=T)
     group = args.group
-    if group > 0 and group < spec.n_req:
+    fused = args.fused and not spec.select_k
+    if group > 0 and group < spec.n_req and not fused:
         step_fn = Hn.PipelinedStep(pool, buf, group)
     else:
         group = -1
 
         def step_fn(n):
-            Hn.decode_step(pool, buf, n)
+            Hn.decode_step(pool, buf, n, fused=fused)
     ss, qs = W.ScoreStream(wl), W.QueryStream(wl)
     host_scores, host_q = [], []
     for n in range(T):
@@ -352,7 +355,9 @@ def main():
                    "kv_dtype": spec.kv_dtype, "heads": spec.heads, "q_per_req": spec.q_per_req,
                    "top_k": Kt, "hot_rows": S, "residency": spec.residency,
                    "step": (f"pipelined over groups of {group} requests on three streams"
-                            if group > 0 else "three entry points in sequence on one stream"),
+                            if group > 0 else
+                            "select_resolve then sparse_mla_decode on one stream" if fused else
+                            "three entry points in sequence on one stream"),
                    **({"growth": "context frozen at the first step's length"}
                       if spec.growth is not None else {}),
                    **({"layers": spec.layers} if spec.layers > 1 else {}),

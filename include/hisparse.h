@@ -311,6 +311,23 @@ hs_status hs_resolve_rows(hs_pool* pool, const int32_t* idx, const int32_t* req_
                           int32_t n_req, int32_t* plan_out, int32_t* counts_out,
                           hipStream_t stream);
 
+/* hs_select_topk followed by hs_resolve_rows in fewer launches: the top-K
+ * filter kernel, then one kernel in which each request's bookkeeping
+ * workgroup first selects its top-K and keeps the selection for the resolve
+ * ([P2] "vLLM GLM 5.3 优化：混合 HiSparse 卸载" §"混合 HiSparse 的技术实现": the
+ * fused kernel handles the top-K results; [P3] §"融合内核与CUDA图兼容"). The
+ * same arguments as the two calls (scores as hs_select_topk, idx_out then
+ * holds the selection, plan_out and counts_out as hs_resolve_rows) and the
+ * same results, bit for bit; the device state advances as after the two
+ * calls. Errors: those of the two calls (HS_DEV_TIMEOUT also covers a copy
+ * workgroup's bounded wait for the selection), and UNSUPPORTED when one
+ * workgroup's LDS (160 KiB) cannot hold the select's tables, the
+ * bookkeeping tables and the selection together (only with a very small
+ * page size and many hot rows; the two calls work there). */
+hs_status hs_select_resolve(hs_pool* pool, const float* scores, int64_t score_stride,
+                            const int32_t* req_ids, int32_t n_req, int32_t* idx_out,
+                            int32_t* plan_out, int32_t* counts_out, hipStream_t stream);
+
 /* Sparse MLA decode attention over the resolved rows ([P3] §"稀疏MLA的核心思想"
  * and its MLA note; [P2] §"与 vLLM 栈的集成", speculative decoding: one
  * resolve plan is replayed for all query tokens of a request).

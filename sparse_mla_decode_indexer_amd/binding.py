@@ -66,6 +66,7 @@ _SIGS = {
     "hs_sparse_mla_decode_union": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _I32, _F32, _VP, _VP, _VP],
     "hs_indexer_scores": [_VP, _VP, _VP, _VP, _I64, _I32, _VP, _I32, _VP, _I64, _VP],
     "hs_resolve_rows": [_VP, _VP, _VP, _I32, _VP, _VP, _VP],
+    "hs_select_resolve": [_VP, _VP, _I64, _VP, _I32, _VP, _VP, _VP, _VP],
     "hs_update_residency": [_VP, _VP, _I32, _VP, _I32, _I32, _VP, _VP, _VP],
     "hs_sparse_mla_decode": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
     "hs_sparse_mla_decode_noalloc": [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _F32, _VP, _VP, _VP],
@@ -170,6 +171,12 @@ def resolve_rows(pool: int, idx: int, req_ids: int, n_req: int, plan_out: int, c
                  stream: int):
     _check(lib().hs_resolve_rows(pool, idx, req_ids, n_req, plan_out, counts_out or None, stream or None),
            "hs_resolve_rows")
+
+
+def select_resolve(pool: int, scores: int, score_stride: int, req_ids: int, n_req: int, idx_out: int,
+                   plan_out: int, counts_out: int, stream: int):
+    _check(lib().hs_select_resolve(pool, scores, score_stride, req_ids, n_req, idx_out, plan_out,
+                                   counts_out or None, stream or None), "hs_select_resolve")
 
 
 def update_residency(pool: int, req_ids: int, n_req: int, budget_pages: int, max_copy_pages: int,

@@ -107,6 +107,14 @@ hs_status set_hip_error(hipError_t e);
 // k = top_k for a plain step.
 hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
                       int32_t n_req, int32_t qsel, int32_t k, int32_t* idx_out, hipStream_t s);
+// The filter kernel of launch_topk alone (one score row per request).
+hs_status launch_topk_filter(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
+                             int32_t n_req, int32_t k, hipStream_t s);
+// Select and resolve in one launch after the filter kernel: idx_out as
+// launch_topk, then plan_out / counts_out as launch_resolve.
+hs_status launch_select_resolve(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
+                                int32_t n_req, int32_t* idx_out, int32_t* plan_out, int32_t* counts_out,
+                                hipStream_t s);
 // Union of the qsel selections of each request (idx [n_req][qsel][k]):
 // union_out [n_req][top_k] ascending, -1 padded; upos_out [n_req][qsel][k]
 // the union position of each selected token (-1 for padding).

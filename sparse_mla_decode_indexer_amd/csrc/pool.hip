@@ -376,6 +376,18 @@ hs_status hs_select_topk_union(hs_pool* pool, const float* scores, int64_t score
   return launch_topk_union(pool, idx_out, n_req, q_per_req, k_per_token, union_out, upos_out, stream);
 }
 
+hs_status hs_select_resolve(hs_pool* pool, const float* scores, int64_t score_stride, const int32_t* req_ids,
+                            int32_t n_req, int32_t* idx_out, int32_t* plan_out, int32_t* counts_out,
+                            hipStream_t stream) {
+  if (!pool || !scores || !req_ids || !idx_out || !plan_out) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req < 0) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req > pool->d.max_batch) return HS_ERR_CAPACITY;
+  if (score_stride < pool->d.max_context || (score_stride & 3)) return HS_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(scores) & 15) return HS_ERR_INVALID_ARGUMENT;
+  if (n_req == 0) return HS_OK;
+  return launch_select_resolve(pool, scores, score_stride, req_ids, n_req, idx_out, plan_out, counts_out, stream);
+}
+
 hs_status hs_indexer_scores(hs_pool* pool, const void* iq, const float* iw, const void* ik, int64_t ik_stride,
                             int32_t n_heads, const int32_t* req_ids, int32_t n_req, float* scores,
                             int64_t score_stride, hipStream_t stream) {

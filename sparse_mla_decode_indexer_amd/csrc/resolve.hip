@@ -48,6 +48,16 @@
 // 32 bits; an entry is rewritten by every launch that covers its batch
 // position, so only one unwritten for 2^32 - 1 launches could alias.)
 //
+// Select and resolve in one launch (hs_select_resolve). The bookkeeper
+// workgroup first runs the request's top-K select (the filter kernel ran
+// before) in the LDS it then reuses, keeps the selection in LDS for the
+// bookkeeping, writes it to idx_out and publishes it by storing the launch's
+// epoch in the position's selection flag once those stores have completed.
+// Copy workgroups wait for that flag (bounded, like their other wait)
+// before they read the selection, with device-coherent loads. This saves
+// the kernel boundary between the two steps and the bookkeeper's reload of
+// the selection.
+//
 // LRU order. lru_order lists all S slots in ascending (stamp, slot). With U
 // the slots hit this step and M misses, the victims are the first M slots of
 // lru_order \ U, and the new order is (lru_order \ U \ victims) followed by
@@ -58,7 +68,7 @@
 
 #include <stdlib.h>
 
-#include "hs_internal.h"
+#include "topk_select.h"
 
 namespace hs {
 
@@ -70,7 +80,8 @@ struct RsScratch {
   uint64_t* mdst;                 // [batch][K] (epoch << 32) | pool row a missed position is copied to, else -1
   int32_t* mslot;                 // [batch][K] hot slot a missed position takes, else -1
   int32_t* mold;                  // [batch][K] token that slot held before (or -1)
-  uint32_t* ctl;                  // [batch][4]: roles handed out, launch sequence (epoch - 1), workgroups done
+  uint32_t* ctl;                  // [batch][4]: roles handed out, launch sequence (epoch - 1), workgroups done,
+                                  // selection published (epoch; select-and-resolve only)
   int parts;                      // ceil(K / kRsPart) copy workgroups per request
 };
 
@@ -89,7 +100,7 @@ __device__ __forceinline__ uint64_t rs_entry(uint32_t epoch, int32_t dst) {
 }
 
 struct RsArgs {
-  const int32_t* idx;
+  const int32_t* idx;             // the selection (select-and-resolve: written by this launch)
   const int32_t* req_ids;
   int n_req;
   int P, Q;    // plan and LRU positions per bookkeeper thread
@@ -101,9 +112,18 @@ struct RsArgs {
   const float* host_scales;
   uint8_t* pool_rows;
   float* pool_scales;
+  // select-and-resolve only: the scores, the top-K scratch and the LDS
+  // offset of the selection (past both the select's and the bookkeeper's LDS)
+  const float* scores;
+  int64_t score_stride;
+  TkScratch tk;
+  int sel_off;
 };
 
 constexpr int kRsPtLds = 8192;  // page-table entries a bookkeeper stages in LDS, at most
+// dynamic LDS of a select-and-resolve workgroup, at most: 160 KiB per
+// workgroup less 4 KiB for the static LDS (RsStatic and the select's tables)
+constexpr size_t kRsFusedMaxDyn = (size_t)156 << 10;
 
 struct RsStatic {
   int tmp[kRsWaves + 1];
@@ -127,11 +147,10 @@ __host__ __device__ inline size_t rs_dyn_bytes(int Spad, int K, int HP, int PT) 
 // per-lane conditions: loop bounds are uniform, LDS tables are padded, and
 // each phase issues all of its LDS reads before using them.
 __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, const RsScratch& sc, RsStatic& st,
-                                         unsigned char* dyn, int i) {
+                                         unsigned char* dyn, int i, const int32_t* sel) {
   const int tid = threadIdx.x;
   const int K = v.top_k, S = v.hot_rows, ps = v.page_size, lps = v.log2_ps, HP = v.hot_pages_per_req;
   const int P = a.P, Q = a.Q, Spad = Q * kRsThreads;
-  const int32_t* sel = a.idx + (size_t)i * K;
   int32_t* plan = a.plan_out + (size_t)i * K;
   const int r0 = a.req_ids[i];
   // What the copy workgroups read (slot, old token, destination) is written
@@ -491,7 +510,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 
 // Copy the missed rows of plan positions [c kRsPart, (c + 1) kRsPart) of
 // request i; wave w takes 4 of them.
-template <int ROW_BYTES, bool FP8>
+template <int ROW_BYTES, bool FP8, bool FUSED>
 __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc,
                                           int i, int c, uint32_t epoch) {
   constexpr int CH = ROW_BYTES / 16;   // 16-byte chunks per row
@@ -504,6 +523,18 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   const int r = valid_req ? r0 : 0;
   const int L = valid_req ? v.ctx_len[r] : 0;
   const int64_t hbase = v.host_base[r];
+  if constexpr (FUSED) {  // wait until this launch's selection of position i is published
+    const uint32_t* flag = sc.ctl + 4 * (size_t)i + 3;
+    int spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      if (++spins > a.spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (spins > a.spin_limit) {
+      if (lane == 0) raise_error(v.error, HS_DEV_TIMEOUT, (uint32_t)i, (uint32_t)j0);
+      return;
+    }
+  }
   // Guess the misses from the current tables. The bookkeeper may be
   // updating them meanwhile (atomic reads, any outcome is harmless): the
   // guess only decides which host reads start before the plan is known.
@@ -511,7 +542,9 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   bool guess = false;
   if (lane < 4) {
     const int j = j0 + lane;
-    t = j < K ? a.idx[(size_t)i * K + j] : -1;
+    t = j >= K ? -1
+        : FUSED ? __hip_atomic_load(&a.idx[(size_t)i * K + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : a.idx[(size_t)i * K + j];
     if (t >= 0 && t < L) {
       const int g = v.page_table[(size_t)r * v.pages_per_req + (t >> lps)];
       const int slot =
@@ -558,6 +591,13 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
     if (lane == 0) raise_error(v.error, HS_DEV_TIMEOUT, (uint32_t)i, (uint32_t)j0);
     return;
   }
+  // A miss destination for a token outside [0, L) can only come from a
+  // selection this wave did not see as the bookkeeper did: raise an error and
+  // copy nothing for it rather than read outside the request's host rows.
+  if (mine && md >= 0 && (t < 0 || t >= L)) {
+    raise_error(v.error, HS_DEV_INDEX_RANGE, (uint32_t)r, (uint32_t)t);
+    md = -1;
+  }
   int ms = -1, mo = -1;
   if (mine) {
     if (md >= 0) {
@@ -602,7 +642,7 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   }
 }
 
-template <int ROW_BYTES, bool FP8>
+template <int ROW_BYTES, bool FP8, bool FUSED>
 __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, RsScratch sc) {
   __shared__ RsStatic st;
   extern __shared__ __align__(16) unsigned char rs_dyn[];
@@ -622,9 +662,23 @@ __global__ __launch_bounds__(kRsThreads) void k_resolve(RsArgs a, StateView v, R
   __syncthreads();
   const int role = st.role;
   if (role == 0) {
-    bookkeep(a, v, sc, st, rs_dyn, i);
+    if constexpr (FUSED) {
+      const int K = v.top_k;
+      int32_t* sel_lds = reinterpret_cast<int32_t*>(rs_dyn + a.sel_off);
+      select_row<true>(a.scores, a.score_stride, a.req_ids, v, a.tk, K, const_cast<int32_t*>(a.idx), i, rs_dyn,
+                       sel_lds);
+      // publish the selection once every thread's idx stores have completed
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+      __syncthreads();  // (also: the select's LDS is free for the bookkeeping)
+      if (tid == 0) __hip_atomic_store(&ctl[3], st.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bookkeep(a, v, sc, st, rs_dyn, i, sel_lds);
+    } else {
+      bookkeep(a, v, sc, st, rs_dyn, i, a.idx + (size_t)i * v.top_k);
+    }
   } else {
-    copy_part<ROW_BYTES, FP8>(a, v, sc, i, role - 1, st.epoch);
+    copy_part<ROW_BYTES, FP8, FUSED>(a, v, sc, i, role - 1, st.epoch);
   }
   // The last workgroup of this position to finish (every other one has
   // taken its ticket and read the sequence by then) prepares the next launch.
@@ -657,8 +711,10 @@ static int pow2_at_least(int x) {
   return p;
 }
 
-hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
-                         int32_t* plan_out, int32_t* counts_out, hipStream_t s) {
+template <bool FUSED>
+static hs_status launch_resolve_impl(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
+                                     int32_t* plan_out, int32_t* counts_out, const float* scores,
+                                     int64_t score_stride, hipStream_t s) {
   StateView v = make_view(p);
   RsScratch sc;
   sc.mdst = reinterpret_cast<uint64_t*>(p->state + p->off.rs_mdst);
@@ -671,23 +727,41 @@ hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids,
            max(4, pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads)),
            v.pages_per_req <= kRsPtLds ? v.pages_per_req : 0, spin_limit(),
            plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
-           p->host_scales, p->pool_rows, p->pool_scales};
-  const size_t dyn =
-      (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req, a.pt_lds) + 15) & ~(size_t)15;
+           p->host_scales, p->pool_rows, p->pool_scales, scores, score_stride, make_tk_scratch(p, 1), 0};
+  size_t dyn = (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req, a.pt_lds) + 15) & ~(size_t)15;
+  if (FUSED) {  // the select's LDS (the bookkeeping reuses it), then the selection
+    if (dyn < kTkSelLdsBytes) dyn = kTkSelLdsBytes;
+    a.sel_off = (int)dyn;
+    dyn += 4 * (size_t)p->d.top_k;
+    if (dyn > kRsFusedMaxDyn) return HS_ERR_UNSUPPORTED;  // (page size too small for one workgroup's LDS)
+  }
   const int grid = n_req * (1 + sc.parts);
   switch (p->d.kv_dtype) {
     case HS_F32:
-      k_resolve<2304, false><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
+      k_resolve<2304, false, FUSED><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
     case HS_BF16:
-      k_resolve<1152, false><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
+      k_resolve<1152, false, FUSED><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
     default:
-      k_resolve<576, true><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
+      k_resolve<576, true, FUSED><<<grid, kRsThreads, dyn, s>>>(a, v, sc);
       break;
   }
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
+}
+
+hs_status launch_resolve(hs_pool* p, const int32_t* idx, const int32_t* req_ids, int32_t n_req,
+                         int32_t* plan_out, int32_t* counts_out, hipStream_t s) {
+  return launch_resolve_impl<false>(p, idx, req_ids, n_req, plan_out, counts_out, nullptr, 0, s);
+}
+
+hs_status launch_select_resolve(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
+                                int32_t n_req, int32_t* idx_out, int32_t* plan_out, int32_t* counts_out,
+                                hipStream_t s) {
+  hs_status st = launch_topk_filter(p, scores, stride, req_ids, n_req, p->d.top_k, s);
+  if (st != HS_OK) return st;
+  return launch_resolve_impl<true>(p, idx_out, req_ids, n_req, plan_out, counts_out, scores, stride, s);
 }
 
 }  // namespace hs

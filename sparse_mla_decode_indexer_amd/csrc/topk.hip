@@ -126,20 +126,22 @@ __global__ __launch_bounds__(kTkSelThreads) void k_topk_select(const float* __re
                                                                const int32_t* __restrict__ req_ids, StateView v,
                                                                TkScratch sc, int K, int32_t* __restrict__ idx_out) {
   extern __shared__ __align__(16) unsigned char tk_dyn[];
-  select_row(scores, stride, req_ids, v, sc, K, idx_out, blockIdx.x, tk_dyn, nullptr);
+  select_row<false>(scores, stride, req_ids, v, sc, K, idx_out, blockIdx.x, tk_dyn, nullptr);
+}
+
+hs_status launch_topk_filter(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
+                             int32_t n_req, int32_t k, hipStream_t s) {
+  StateView v = make_view(p);
+  TkScratch sc = make_tk_scratch(p, 1);
+  k_topk_filter<<<dim3(sc.max_chunks, n_req), kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc, k);
+  HS_HIP_CHECK(hipGetLastError());
+  return HS_OK;
 }
 
 hs_status launch_topk(hs_pool* p, const float* scores, int64_t stride, const int32_t* req_ids,
                       int32_t n_req, int32_t qsel, int32_t k, int32_t* idx_out, hipStream_t s) {
   StateView v = make_view(p);
-  TkScratch sc;
-  sc.count = reinterpret_cast<int32_t*>(p->state + p->off.tk_count);
-  sc.maxk = reinterpret_cast<uint32_t*>(p->state + p->off.tk_max);
-  sc.cand = reinterpret_cast<uint2*>(p->state + p->off.tk_cand);
-  sc.bound = reinterpret_cast<uint32_t*>(p->state + p->off.tk_bound);
-  sc.max_chunks = (p->d.max_context + kTkChunk - 1) / kTkChunk;
-  sc.qsel = qsel;
-  sc.bound_q = p->off.sel_q;
+  TkScratch sc = make_tk_scratch(p, qsel);
   const int rows = n_req * qsel;
   k_topk_filter<<<dim3(sc.max_chunks, rows), kTkThreads, 0, s>>>(scores, stride, req_ids, v, sc, k);
   k_topk_select<<<rows, kTkSelThreads, kTkSelLdsBytes, s>>>(scores, stride, req_ids, v, sc, k, idx_out);

@@ -54,8 +54,30 @@ constexpr int kTkOffEntries = kTkMaxChunks + 4;  // kTkMaxChunks + 1, rounded up
 constexpr size_t kTkSelHistBytes = 3 * (size_t)kTkBins * 4;
 constexpr size_t kTkSelLdsBytes = kTkSelHistBytes + 8 * (size_t)kTkOffEntries + 8 * (size_t)kTkStage;
 
+// Views of the top-K scratch of a pool for a call with qsel score rows per
+// request (host side).
+inline TkScratch make_tk_scratch(const hs_pool* p, int qsel) {
+  TkScratch sc;
+  sc.count = reinterpret_cast<int32_t*>(p->state + p->off.tk_count);
+  sc.maxk = reinterpret_cast<uint32_t*>(p->state + p->off.tk_max);
+  sc.cand = reinterpret_cast<uint2*>(p->state + p->off.tk_cand);
+  sc.bound = reinterpret_cast<uint32_t*>(p->state + p->off.tk_bound);
+  sc.max_chunks = (p->d.max_context + kTkChunk - 1) / kTkChunk;
+  sc.qsel = qsel;
+  sc.bound_q = p->off.sel_q;
+  return sc;
+}
+
+// COHERENT: the store is device-coherent (agent scope), for a selection
+// that workgroups of the same launch read (plain stores reach only this
+// XCD's L2 until the kernel ends).
+template <bool COHERENT>
 __device__ inline void out_store(int32_t* idx_out, int i, int K, int j, int32_t tok) {
-  idx_out[(size_t)i * K + j] = tok;
+  int32_t* p = idx_out + (size_t)i * K + j;
+  if constexpr (COHERENT)
+    __hip_atomic_store(p, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = tok;
 }
 
 // Block-wide search of a 4096-bin histogram from the top bin down: for each
@@ -100,7 +122,10 @@ __device__ void hist_find2(const uint32_t* h, int need0, int need1, int* wtot, F
 
 // Select of score row i (one 1,024-thread workgroup). `lds` is
 // kTkSelLdsBytes of LDS, 16-byte aligned; sel_lds, when given, receives
-// the selected tokens as idx_out does (K entries).
+// the selected tokens as idx_out does (K entries). COHERENT: idx_out is
+// written with device-coherent stores (read by other workgroups of the
+// same launch).
+template <bool COHERENT>
 __device__ __forceinline__ void select_row(const float* __restrict__ scores, int64_t stride,
                                            const int32_t* __restrict__ req_ids, const StateView& v,
                                            const TkScratch& sc, int K, int32_t* __restrict__ idx_out, int i,
@@ -116,7 +141,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ scores, int
   __shared__ FindOut fres;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto put = [&](int j, int32_t tok) {
-    out_store(idx_out, i, K, j, tok);
+    out_store<COHERENT>(idx_out, i, K, j, tok);
     if (sel_lds) sel_lds[j] = tok;
   };
   const int qi = i / sc.qsel, qt = i - qi * sc.qsel;  // request position, query token

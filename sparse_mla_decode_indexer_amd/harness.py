@@ -123,8 +123,9 @@ class StepBuffers:
             self.q[n].copy_(torch.from_numpy(q))
 
 
-def decode_step(pool: TieredPool, buf: StepBuffers, n: int = 0):
-    """One step: top-K -> resolve -> sparse MLA attention (stream-ordered).
+def decode_step(pool: TieredPool, buf: StepBuffers, n: int = 0, fused: bool = False):
+    """One step: top-K -> resolve -> sparse MLA attention (stream-ordered);
+    with `fused`, top-K and resolve run as hs_select_resolve (same results).
     A speculative step with a selection per query token selects per token,
     resolves the union (buf.idx) once and attends per token through it."""
     if buf.union:
@@ -132,8 +133,11 @@ def decode_step(pool: TieredPool, buf: StepBuffers, n: int = 0):
         pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
         pool.sparse_mla_decode_union(buf.q[n], buf.plan, buf.upos, buf.sm_scale, buf.out, buf.lse)
         return
-    pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
-    pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
+    if fused:
+        pool.select_resolve(buf.scores[n], buf.req_ids, buf.idx, buf.plan, buf.counts)
+    else:
+        pool.select_topk(buf.scores[n], buf.req_ids, buf.idx)
+        pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
     pool.sparse_mla_decode(buf.q[n], buf.plan, buf.sm_scale, buf.out, buf.lse)
 
 

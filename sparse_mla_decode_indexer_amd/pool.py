@@ -134,6 +134,12 @@ class TieredPool:
         B.resolve_rows(self.handle, idx.data_ptr(), req_ids.data_ptr(), int(req_ids.numel()),
                        plan_out.data_ptr(), _ptr(counts_out), _stream())
 
+    def select_resolve(self, scores: torch.Tensor, req_ids: torch.Tensor, idx_out: torch.Tensor,
+                       plan_out: torch.Tensor, counts_out: Optional[torch.Tensor] = None):
+        """select_topk then resolve_rows, fused (same results)."""
+        B.select_resolve(self.handle, scores.data_ptr(), scores.stride(0), req_ids.data_ptr(), int(req_ids.numel()),
+                         idx_out.data_ptr(), plan_out.data_ptr(), _ptr(counts_out), _stream())
+
     def sparse_mla_decode(self, q: torch.Tensor, plan: torch.Tensor, sm_scale: float,
                           out: torch.Tensor, lse: Optional[torch.Tensor] = None):
         n_req, q_per_req, n_heads, _ = q.shape

@@ -122,7 +122,7 @@ class Runner:
     """One workload on one pool, stepped in lockstep with the oracle."""
 
     def __init__(self, wl: W.Workload, check_state: bool = True, sharded: bool = False,
-                 group: Optional[int] = None):
+                 group: Optional[int] = None, fused: bool = False):
         self.wl = wl
         self.spec = wl.spec
         self.pool = Hn.make_pool(wl)
@@ -130,6 +130,7 @@ class Runner:
         self.buf = Hn.StepBuffers(wl)
         # group: run each step as the pipelined step over groups of this many requests
         self.pipe = Hn.PipelinedStep(self.pool, self.buf, group) if group else None
+        self.fused = fused  # top-K and resolve as one call (hs_select_resolve)
         self.oracle = ShardedOracle(wl) if sharded else make_oracle(wl)
         self.scores = W.ScoreStream(wl)
         self.queries = W.QueryStream(wl)
@@ -164,7 +165,7 @@ class Runner:
         if self.pipe is not None:
             self.pipe(0)
         else:
-            Hn.decode_step(self.pool, self.buf)
+            Hn.decode_step(self.pool, self.buf, fused=self.fused)
         torch.cuda.synchronize()
         ref = self.oracle.step(sc, None, lens, with_attention=False)
         self.n += 1

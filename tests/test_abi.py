@@ -17,7 +17,7 @@ def _lib():
 def test_exports_every_declared_function():
     L = _lib()
     names = B.header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert set(B._SIGS) == set(names)

@@ -18,7 +18,12 @@ def test_traffic_summaries_are_well_formed():
     for n in names:
         with open(os.path.join(prof, n)) as f:
             t = json.load(f)
-        assert t["source_files"] == sorted(bench.STEP_SOURCES), n
+        # a summary taken on the current sources names exactly them; an older
+        # one names files of the tree (bench.py reports its traffic as null)
+        if t["source_sha256"] == bench.source_sha256():
+            assert t["source_files"] == sorted(bench.STEP_SOURCES), n
+        for p in t["source_files"]:
+            assert os.path.exists(os.path.join(bench.ROOT, p)), (n, p)
         assert t["bytes_per_write_kib"] > 0 and t["bytes_per_fetch_kib"] > 0, n
         for k in ("k_topk_filter", "k_topk_select"):
             assert k in t["kernels"], (n, k)

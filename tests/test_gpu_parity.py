@@ -672,3 +672,48 @@ def test_resolve_wait_that_gives_up_then_hot_reset_is_exact(monkeypatch):
             rn.step(heads=[0, 77])
     finally:
         rn.close()
+
+
+FUSED_CASES = [
+    ("single-128k", dict(ctx=20000, host_pages=240, steps=6)),
+    ("batch32", dict(n_req=7, ctx_range=(4096, 40000), steps=5)),
+    ("single-1m-fp8", dict(ctx=30000, host_pages=400, steps=6)),
+    ("tiny", dict(steps=4)),
+    ("batch32", dict(n_req=3, ctx_range=(600, 1500), steps=3)),  # L < K for every request
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(FUSED_CASES)])
+def test_select_resolve_fused(name, kw):
+    """hs_select_resolve (top-K and resolve in one launch after the filter)
+    gives the same selection, plan, counts and device state as the two
+    calls, bit for bit against the oracle, cold and warm steps; bf16, fp8
+    and fp32 pools, mixed residency, contexts shorter than K."""
+    spec = small(name, **kw)
+    log(f"[gpu] select+resolve fused: {name} {kw}")
+    wl = W.generate(spec)
+    rn = Runner(wl, fused=True)
+    try:
+        for _ in range(spec.steps):
+            rn.step(heads=[0, 5])
+    finally:
+        rn.close()
+
+
+def test_select_resolve_fused_bad_request_id():
+    spec = small("batch32", n_req=3, ctx_range=(4096, 9000), steps=2)
+    wl = W.generate(spec)
+    rn = Runner(wl, fused=True)
+    try:
+        rn.step()
+        buf = rn.buf
+        bad = torch.tensor([0, 77, 2], dtype=torch.int32, device="cuda")
+        buf.idx.fill_(5)
+        buf.plan.fill_(5)
+        rn.pool.select_resolve(buf.scores[0], bad, buf.idx, buf.plan, buf.counts)
+        torch.cuda.synchronize()
+        code = rn.pool.device_error()
+        assert code[0] == 4 and code[1] == 1 and code[2] == 77, code
+        assert (buf.idx[1] == -1).all() and (buf.plan[1] == -1).all() and (buf.counts[1] == 0).all()
+    finally:
+        rn.close()
