@@ -40,7 +40,9 @@
 //     register transposes of row-major LDS reads, in the same row order as
 //     P^T;
 //   - two workgroup barriers per tile: tile landed / previous tile retired,
-//     and the partial-score exchange.
+//     and the partial-score exchange; the gather of tile t + 2 is issued one
+//     DMA at a time between the QK MFMAs of tile t;
+//   - output rows leave through LDS so that each store writes whole lines.
 // Softmax is online (fp32, base 2): a reference maximum that moves only
 // when a score passes it by more than 2^8, and a running sum. With more than
 // one split, each split writes a normalised partial output and its
@@ -87,7 +89,7 @@ constexpr uint64_t kBufMaxBytes = 0xFFFF0000ull;
 constexpr uint32_t kBufOob = 0xFFFF0000u;  // offset past any buffer view
 constexpr int kBufWord3 = 0x00020000;      // descriptor word 3: 32-bit data format
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
 constexpr int kPvAhead = 3;  // V^T operand blocks loaded ahead of their MFMAs
 constexpr int kQkAhead = 3;  // K operand steps loaded ahead of their MFMAs
 
@@ -364,8 +366,6 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt) {
     __builtin_amdgcn_s_waitcnt(kWaitOne);  // this wave's part of tile t has landed
     lds_sync();                            // all of tile t is in LDS; tile t-1 is done
-    issue(rows_next, nxt);
-    rows_of(t + 3, rows_next);
     const uint8_t* T = FP8 ? wide : cur;
     if (FP8) {  // widen the raw codes of tile t into the bf16 tile
       for (int x = tid; x < kTile * kRawChunks; x += kAttThreads) {
@@ -381,6 +381,11 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       }
       lds_sync();
     }
+    // The gather of tile t + 2 goes out between the QK MFMAs below (one
+    // DMA per key step): the CU's texture path moves a tile in about as
+    // long as the QK phase takes, and DMAs issued all at once, by every
+    // wave after the barrier, stalled the issuing waves until it drained.
+    issue(rows_next, nxt);
     // QK partial over key dims 288*half .. +288, all 32 rows of the tile
     // (operand addresses: one per-lane base plus constant offsets)
     f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -401,7 +406,9 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     for (int kk = 0; kk < kKSteps; ++kk) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
       if (kk + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      if (kk < kIssue) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
     }
+    rows_of(t + 3, rows_next);
     if constexpr (FP8) {  // undo the query half's power-of-two scale (exact)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -538,25 +545,45 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 
   // softmax denominator: sum over the 4 lanes (row groups) of each query
   const float l = sum_across_kg(lpart);
-  if (!qvalid) return;
+  lds_sync();  // every wave is past its last tile: the tile buffers are free
   const float inv = l > 0.f ? sref / l : 0.f;  // (sref = 1 for bf16 rows)
   const float lse2 = l > 0.f ? m_run + __log2f(l) : -INFINITY;
-  float* dst;
-  if (n_splits == 1) {
-    dst = out + ((size_t)i * QR + qh) * kNope;
-    if (lse_out && kg == 0 && half == 0) lse_out[(size_t)i * QR + qh] = lse2 * kLn2;
-  } else {
-    const size_t prow = ((size_t)i * n_splits + sp) * QR + qh;
-    dst = part_o + prow * kNope;
-    if (kg == 0 && half == 0) part_lse[prow] = lse2;
+  if (qvalid && kg == 0 && half == 0) {
+    if (n_splits == 1) {
+      if (lse_out) lse_out[(size_t)i * QR + qh] = lse2 * kLn2;
+    } else {
+      part_lse[((size_t)i * n_splits + sp) * QR + qh] = lse2;
+    }
   }
-  // lane holds dims 256*half + 16b + 4kg + v, v = 0..3; streaming stores
-  // (read once, by the merge kernel or the caller): fewer dirty L2 lines to
-  // write back when the kernel ends
+  // Output rows go out through this wave's own LDS region, 64 dims at a
+  // time: lane (kg, ln) deposits dims 16b + 4kg .. +4 of query ln, then each
+  // lane takes 16 contiguous bytes of one query, so that every store
+  // instruction writes 256 contiguous bytes (whole cache lines) of each of
+  // 4 rows. Streaming stores: the rows are read once, by the merge kernel
+  // or the caller.
+  constexpr int kStgRow = 272;  // a query's 64 dims (256 bytes) + 16 (LDS banks)
+  static_assert(2 * QB * 16 * kStgRow <= (FP8 ? kTileBytes : kBufBytes), "staging fits the tile buffer");
+  uint8_t* stg = (FP8 ? wide : bufA) + wave * 16 * kStgRow;
+  const size_t row0 = n_splits == 1 ? (size_t)i * QR : ((size_t)i * n_splits + sp) * QR;
+  float* const dst = n_splits == 1 ? out : part_o;
 #pragma unroll
-  for (int b = 0; b < 16; ++b)
-    __builtin_nontemporal_store(f32x4_t{acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv},
-                                reinterpret_cast<f32x4_t*>(dst + 256 * half + 16 * b + 4 * kg));
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const f32x4_t x = acc[4 * p + bb];
+      *reinterpret_cast<f32x4_t*>(stg + ln * kStgRow + (16 * bb + 4 * kg) * 4) =
+          f32x4_t{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ql = 4 * r + (lane >> 4);  // query of this lane's 16 bytes
+      const f32x4_t y = *reinterpret_cast<const f32x4_t*>(stg + ql * kStgRow + (lane & 15) * 16);
+      const int qh2 = hg * kQPerWG + qb * 16 + ql;
+      if (qh2 < QR)
+        __builtin_nontemporal_store(
+            y, reinterpret_cast<f32x4_t*>(dst + (row0 + qh2) * kNope + 256 * half + 64 * p + 4 * (lane & 15)));
+    }
+  }
 }
 
 // Merge split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
