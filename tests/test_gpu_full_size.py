@@ -11,7 +11,8 @@ is compared within 2e-3 of the fp64 oracle on every head at the first step,
 at the turn boundaries named below and at the last step, and on a sample of
 heads (every query token of every request) at every other step.
 
-Schedules:
+Schedules (single-128k and batch32 also with top-K and resolve as one
+call, hs_select_resolve):
   single-128k        64 steps
   batch32            32 steps
   single-1m-fp8      128 steps (every score redrawn at each topic-shift step;
@@ -45,13 +46,27 @@ FULL = [
 
 @pytest.mark.parametrize("name,heads,full_steps", FULL, ids=[f[0] for f in FULL])
 def test_full_size_whole_schedule(name, heads, full_steps):
+    _whole_schedule(name, heads, full_steps, fused=False)
+
+
+# hs_select_resolve (top-K and resolve in one call) on the two workloads
+# whose steps it is timed on (bench.py --fused)
+FUSED = [f for f in FULL if f[0] in ("single-128k", "batch32")]
+
+
+@pytest.mark.parametrize("name,heads,full_steps", FUSED, ids=[f[0] for f in FUSED])
+def test_full_size_whole_schedule_select_resolve(name, heads, full_steps):
+    _whole_schedule(name, heads, full_steps, fused=True)
+
+
+def _whole_schedule(name, heads, full_steps, fused):
     spec = W.SPECS[name]
     steps = spec.steps
-    log(f"[gpu] full size {name}: all {steps} steps, sampled heads {heads}, every head at "
-        f"1, {full_steps}, {steps}")
+    log(f"[gpu] full size {name}{' (select_resolve)' if fused else ''}: all {steps} steps, sampled heads "
+        f"{heads}, every head at 1, {full_steps}, {steps}")
     t0 = time.time()
     wl = W.generate(spec)
-    rn = Runner(wl, sharded=True)
+    rn = Runner(wl, sharded=True, fused=fused)
     if spec.growth is not None:
         rn.incremental = True          # the engine sets only the pages entering the context
     try:

@@ -636,25 +636,28 @@ def test_pipelined_step_over_request_groups(group):
         rn.close()
 
 
-def test_resolve_wait_that_gives_up_then_hot_reset_is_exact(monkeypatch):
+@pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "select_resolve"])
+def test_resolve_wait_that_gives_up_then_hot_reset_is_exact(monkeypatch, fused):
     """A copy wave whose bounded wait gives up raises HS_DEV_TIMEOUT (batch
     and plan position in range) instead of hanging; after clearing the error
     and resetting the hot buffers (the documented recovery) the following
     steps are bit-exact with the oracle, so no destination published late by
     the call that gave up is taken by a later call (each carries its call's
     epoch). The wait is made to give up with HS_RESOLVE_SPIN_LIMIT=0 (one
-    poll); whether it does depends on timing, and both outcomes are checked."""
+    poll); whether it does depends on timing, and both outcomes are checked.
+    With top-K and resolve as one call the copy waves' first wait is for the
+    selection, published by the bookkeeper after its select."""
     spec = small("batch32", n_req=8, ctx_range=(8192, 40000), steps=5)
-    log("[gpu] resolve wait giving up (spin limit 0), then hot reset")
+    log(f"[gpu] resolve wait giving up (spin limit 0), then hot reset; fused {fused}")
     wl = W.generate(spec)
-    rn = Runner(wl)
+    rn = Runner(wl, fused=fused)
     try:
         rn.step()
         monkeypatch.setenv("HS_RESOLVE_SPIN_LIMIT", "0")
         lens = rn.sched[rn.n]
         sc, q = rn.scores.next(lens), rn.queries.next()
         rn.buf.upload(0, sc, q)
-        Hn.decode_step(rn.pool, rn.buf)
+        Hn.decode_step(rn.pool, rn.buf, fused=fused)
         torch.cuda.synchronize()
         rn.oracle.step(sc, None, lens, with_attention=False)
         rn.n += 1

@@ -101,11 +101,13 @@ def test_union_full_size_first_turns():
         rn.close()
 
 
-def _graph_vs_eager(spec, step_fn, replays=4):
+def _graph_vs_eager(spec, step_fn, replays=4, eager_fn=None):
     """Capture one step in a hipGraph on pool B and replay it `replays`
     times, with new inputs copied in eagerly between the replays; the same
-    steps run eagerly on twin pool A. Every replay's outputs and the final
-    LRU state must be bit-identical to the eager run."""
+    steps run eagerly on twin pool A (through eager_fn when given). Every
+    replay's outputs and the final LRU state must be bit-identical to the
+    eager run."""
+    eager_fn = eager_fn or step_fn
     from sparse_mla_decode_indexer_amd import harness as Hn
     wl_a, wl_b = W.generate(spec), W.generate(spec)
     pa, pb = Hn.make_pool(wl_a), Hn.make_pool(wl_b)
@@ -129,7 +131,7 @@ def _graph_vs_eager(spec, step_fn, replays=4):
                 bb.upload(0, sc, q)
             torch.cuda.synchronize()
             g.replay()
-            step_fn(pa, ba)
+            eager_fn(pa, ba)
             torch.cuda.synchronize()
             for name in ("idx", "plan", "counts", "out", "lse") + (("sel", "upos") if spec.select_k else ()):
                 assert torch.equal(getattr(ba, name), getattr(bb, name)), f"replay {n}: {name}"
@@ -158,3 +160,14 @@ def test_noalloc_attention_graph_replays_match_eager():
         pool.resolve_rows(buf.idx, buf.req_ids, buf.plan, buf.counts)
         pool.sparse_mla_decode_noalloc(buf.q[0], buf.plan, buf.sm_scale, buf.out, buf.lse)
     _graph_vs_eager(small("batch32", n_req=3, ctx_range=(8192, 30000), steps=4), step)
+
+
+def test_select_resolve_step_graph_replays_match_two_calls():
+    """A step with top-K and resolve as one call (hs_select_resolve), captured
+    in a hipGraph and replayed with new inputs, against the same steps run
+    eagerly as separate top-K and resolve calls."""
+    log("[gpu] select_resolve step: hipGraph replays vs eager two-call steps")
+    from sparse_mla_decode_indexer_amd import harness as Hn
+    _graph_vs_eager(small("batch32", n_req=5, ctx_range=(4096, 40000), steps=4),
+                    lambda pool, buf: Hn.decode_step(pool, buf, 0, fused=True),
+                    eager_fn=lambda pool, buf: Hn.decode_step(pool, buf, 0))
