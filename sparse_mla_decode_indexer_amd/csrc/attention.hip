@@ -74,7 +74,6 @@ constexpr int kRowChunks = kChunks + 1;          // LDS row stride: 73 chunks (o
 constexpr int kTilePos = kTile * kRowChunks;     // 2336 chunk positions per tile
 constexpr int kTileBytes = kTilePos * 16;        // 37376
 constexpr int kRawChunks = kRowDim / 16;         // 36 chunks per fp8 row
-constexpr int kRawTileBytes = kTile * kRawChunks * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.f;  // see the online softmax in k_attn_mfma

@@ -152,6 +152,17 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   const int K = v.top_k, S = v.hot_rows, ps = v.page_size, lps = v.log2_ps, HP = v.hot_pages_per_req;
   const int P = a.P, Q = a.Q, Spad = Q * kRsThreads;
   int32_t* plan = a.plan_out + (size_t)i * K;
+  // this thread's selected tokens: read together with the request id (their
+  // addresses do not depend on it)
+  int tok[kRsPos];
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) {
+    if (e < P) {
+      const int j = e * kRsThreads + tid;
+      const int t = sel[min(j, K - 1)];
+      tok[e] = j < K ? t : -1;
+    }
+  }
   const int r0 = a.req_ids[i];
   // What the copy workgroups read (slot, old token, destination) is written
   // with device-coherent stores; a position's destination goes out (from
@@ -203,7 +214,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   int32_t* ptl = hp + HP;
   uint8_t* flag = reinterpret_cast<uint8_t*>(ptl + a.pt_lds);
   const int npg = (L + ps - 1) >> lps;  // pages of the context
-  const bool pt_in_lds = npg > 0 && npg <= a.pt_lds;
+  // The request's whole page table is staged when it fits (a.pt_lds is then
+  // pages_per_req), so that neither the staging nor the reverse-map lookups
+  // below wait for the context length: lookups are clamped to the request's
+  // rows of the tables, and the length only enters the classification.
+  const bool pt_in_lds = a.pt_lds > 0;
 
   // 0. loads: LRU order and slot tags (coalesced, then to LDS), hot pages;
   //    this thread's selected tokens, then their page-table and reverse-map
@@ -238,11 +253,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   }
   for (int p = tid; p < HP; p += kRsThreads) hp[p] = hp_g[p];
   if (pt_in_lds)
-    for (int p = tid; p < npg; p += kRsThreads) ptl[p] = pt[p];
+    for (int p = tid; p < a.pt_lds; p += kRsThreads) ptl[p] = pt[p];
   if (tid == 0) st.n_res = st.n_hot = 0;
   const int lane = tid & 63, wave = tid >> 6;
   const unsigned long long below = (1ull << lane) - 1ull;
-  int tok[kRsPos], code[kRsPos];  // code: pool row, -1 nothing, -2 miss
+  int code[kRsPos];  // code: pool row, -1 nothing, -2 miss
   uint32_t missbits = 0u;  // bit e: position e of this thread is a miss
   unsigned long long mb[kRsPos];  // miss bits of this wave's 64 positions of each e
   int M;
@@ -251,16 +266,8 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
-        const int j = e * kRsThreads + tid;
-        const int t = sel[min(j, K - 1)];
-        tok[e] = j < K ? t : -1;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < kRsPos; ++e) {
-      if (e < P) {
         const int t = tok[e];
-        const int tt = (t >= 0 && t < L) ? t : 0;  // an in-range address either way
+        const int tt = (t >= 0 && t < v.max_context) ? t : 0;  // an address inside the request's rows
         if (!pt_in_lds) g[e] = pt[tt >> lps];
         sl[e] = rev[tt];
       }
@@ -274,7 +281,7 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     for (int e = 0; e < kRsPos; ++e) {
       if (e < P) {
         const int t = tok[e];
-        const int tt = (t >= 0 && t < L) ? t : 0;
+        const int tt = (t >= 0 && t < v.max_context) ? t : 0;
         if (pt_in_lds) g[e] = ptl[tt >> lps];
         hpg[e] = hp[min(max(sl[e], 0), S - 1) >> lps];
       }
@@ -323,72 +330,81 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
     __syncthreads();
     M = st.tmp[0];
   }
+  // A request whose selected tokens are all resident touches no slot: its
+  // LRU order, tags and stamps stay as they are, so steps 2 and 3 and the
+  // LRU part of step 5 are skipped (a uniform branch). Without misses the
+  // victim slots are not looked up either.
+  const bool touched = M > 0 || st.n_hot > 0;
   // 2. untouched slots in LRU order (thread t holds LRU positions [tQ, tQ+Q));
   //    the first M of them are the victims
   int my[kRsSlots];
   uint32_t km = 0u;  // bit e: my[e] is untouched
+  uint32_t fm = 0u;  // bit e: slot tQ + e is fresh (hit or victim)
+  int kept = 0, kbase = 0, fbase = 0;
+  if (touched) {
 #pragma unroll
-  for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
-    if (4 * e4 < Q) {
-      const int4 x = reinterpret_cast<const int4*>(lru + tid * Q)[e4];
-      my[4 * e4] = x.x;
-      my[4 * e4 + 1] = x.y;
-      my[4 * e4 + 2] = x.z;
-      my[4 * e4 + 3] = x.w;
-    }
-  }
-  {
-    int fl[kRsSlots];
-#pragma unroll
-    for (int e = 0; e < kRsSlots; ++e) {
-      if (e < Q) {
-        const int s = max(my[e], 0);
-        fl[e] = flag[s];
+    for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+      if (4 * e4 < Q) {
+        const int4 x = reinterpret_cast<const int4*>(lru + tid * Q)[e4];
+        my[4 * e4] = x.x;
+        my[4 * e4 + 1] = x.y;
+        my[4 * e4 + 2] = x.z;
+        my[4 * e4 + 3] = x.w;
       }
     }
+    {
+      int fl[kRsSlots];
 #pragma unroll
-    for (int e = 0; e < kRsSlots; ++e) {
-      if (e < Q) {
-        km |= (my[e] >= 0 && !(fl[e] & 1)) ? (1u << e) : 0u;
+      for (int e = 0; e < kRsSlots; ++e) {
+        if (e < Q) {
+          const int s = max(my[e], 0);
+          fl[e] = flag[s];
+        }
       }
-    }
-  }
-  int kept;
-  const int kbase = block_excl_sum(__popc(km), st.tmp, kept);
-  // 3. victims (LDS)
-  {
-    int kpos = kbase;
 #pragma unroll
-    for (int e = 0; e < kRsSlots; ++e) {
-      if (e < Q) {
-        if ((km >> e) & 1u) {
-          if (kpos < M) {
-            vic[kpos] = my[e];
-            flag[my[e]] |= 2;
-          }
-          ++kpos;
+      for (int e = 0; e < kRsSlots; ++e) {
+        if (e < Q) {
+          km |= (my[e] >= 0 && !(fl[e] & 1)) ? (1u << e) : 0u;
         }
       }
     }
-  }
-  __syncthreads();
-  // fresh slots (hit or victim) of this thread's slot range [tQ, tQ + Q)
-  uint32_t fm = 0u;
+    kbase = block_excl_sum(__popc(km), st.tmp, kept);
+    // 3. victims (LDS)
+    {
+      int kpos = kbase;
 #pragma unroll
-  for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
-    if (4 * e4 < Q) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(flag + tid * Q)[e4];
-      fm |= ((w & 0xFFu) ? 1u : 0u) << (4 * e4);
-      fm |= ((w & 0xFF00u) ? 1u : 0u) << (4 * e4 + 1);
-      fm |= ((w & 0xFF0000u) ? 1u : 0u) << (4 * e4 + 2);
-      fm |= ((w & 0xFF000000u) ? 1u : 0u) << (4 * e4 + 3);
+      for (int e = 0; e < kRsSlots; ++e) {
+        if (e < Q) {
+          if ((km >> e) & 1u) {
+            if (kpos < M) {
+              vic[kpos] = my[e];
+              flag[my[e]] |= 2;
+            }
+            ++kpos;
+          }
+        }
+      }
     }
-  }
-  int ftot;
-  const int fbase = (kept - M) + block_excl_sum(__popc(fm), st.tmp, ftot);
+    __syncthreads();
+    // fresh slots (hit or victim) of this thread's slot range [tQ, tQ + Q)
+#pragma unroll
+    for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+      if (4 * e4 < Q) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(flag + tid * Q)[e4];
+        fm |= ((w & 0xFFu) ? 1u : 0u) << (4 * e4);
+        fm |= ((w & 0xFF00u) ? 1u : 0u) << (4 * e4 + 1);
+        fm |= ((w & 0xFF0000u) ? 1u : 0u) << (4 * e4 + 2);
+        fm |= ((w & 0xFF000000u) ? 1u : 0u) << (4 * e4 + 3);
+      }
+    }
+    int ftot;
+    fbase = (kept - M) + block_excl_sum(__popc(fm), st.tmp, ftot);
+  }  // touched
   // the i-th miss takes the i-th victim
   int vs[kRsPos];
-  {
+#pragma unroll
+  for (int e = 0; e < kRsPos; ++e) vs[e] = -1;
+  if (M > 0) {
     int hv[kRsPos];
 #pragma unroll
     for (int e = 0; e < kRsPos; ++e) {
@@ -434,38 +450,40 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
   //    new order is assembled in LDS (the old one there is no longer read)
   //    and written out with coalesced 16-byte stores.
   {
-    int kpos = kbase;
+    if (touched) {
+      int kpos = kbase;
 #pragma unroll
-    for (int e = 0; e < kRsSlots; ++e) {
-      if (e < Q) {
-        if ((km >> e) & 1u) {
-          if (kpos >= M) lru[kpos - M] = my[e];
-          ++kpos;
+      for (int e = 0; e < kRsSlots; ++e) {
+        if (e < Q) {
+          if ((km >> e) & 1u) {
+            if (kpos >= M) lru[kpos - M] = my[e];
+            ++kpos;
+          }
         }
       }
-    }
-    int fpos = fbase;
+      int fpos = fbase;
 #pragma unroll
-    for (int e = 0; e < kRsSlots; ++e) {
-      if (e < Q && ((fm >> e) & 1u)) {
-        const int s = tid * Q + e;
-        lru[fpos++] = s;
-        if (!stamp4) stamp[s] = n;
+      for (int e = 0; e < kRsSlots; ++e) {
+        if (e < Q && ((fm >> e) & 1u)) {
+          const int s = tid * Q + e;
+          lru[fpos++] = s;
+          if (!stamp4) stamp[s] = n;
+        }
       }
-    }
 #pragma unroll
-    for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
-      const int x = tid * Q + 4 * e4;
-      if (4 * e4 < Q && stamp4 && x < S) {
-        int4 w = st4[e4];
-        const uint32_t f = fm >> (4 * e4);
-        w.x = (f & 1u) ? n : w.x;
-        w.y = (f & 2u) ? n : w.y;
-        w.z = (f & 4u) ? n : w.z;
-        w.w = (f & 8u) ? n : w.w;
-        reinterpret_cast<int4*>(stamp)[x >> 2] = w;
+      for (int e4 = 0; e4 < kRsSlots / 4; ++e4) {
+        const int x = tid * Q + 4 * e4;
+        if (4 * e4 < Q && stamp4 && x < S) {
+          int4 w = st4[e4];
+          const uint32_t f = fm >> (4 * e4);
+          w.x = (f & 1u) ? n : w.x;
+          w.y = (f & 2u) ? n : w.y;
+          w.z = (f & 4u) ? n : w.z;
+          w.w = (f & 8u) ? n : w.w;
+          reinterpret_cast<int4*>(stamp)[x >> 2] = w;
+        }
       }
-    }
+    }  // touched
     // (the victims' tags and the reverse map are updated by the copy
     // workgroups, which hold each miss's token, slot and the slot's old token)
     // page recency for the residency manager: every page the indexer
@@ -484,7 +502,9 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
       }
     }
     __syncthreads();  // new order and page marks in LDS
-    if ((S & 3) == 0) {
+    if (!touched) {
+      // (the LRU order is unchanged)
+    } else if ((S & 3) == 0) {
       for (int x = tid; x < S / 4; x += kRsThreads)
         reinterpret_cast<int4*>(order)[x] = reinterpret_cast<const int4*>(lru)[x];
     } else {
@@ -540,6 +560,7 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
   // guess only decides which host reads start before the plan is known.
   int t = -1;
   bool guess = false;
+  bool settled = true;  // this position is certainly no miss: padding, out of range or on a resident page
   if (lane < 4) {
     const int j = j0 + lane;
     t = j >= K ? -1
@@ -550,8 +571,14 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
       const int slot =
           __hip_atomic_load(&v.rev[(size_t)r * v.max_context + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       guess = g < 0 && slot < 0;
+      settled = g >= 0;
     }
   }
+  // The page table does not change during a call, so the bookkeeper
+  // classifies a position on a resident page (and padding) exactly as this
+  // wave does: no copy. A wave with nothing but such positions is done
+  // without waiting for the plan.
+  if ((__ballot(settled) & 0xFull) == 0xFull) return;
   const unsigned gb = (unsigned)(__ballot(guess) & 0xFull);
   int tk[4];
 #pragma unroll
