@@ -138,6 +138,10 @@ typedef struct hs_pool_sizes {
   size_t host_store_bytes;   /* pinned host memory hs_init_pool allocates */
   int32_t hot_rows;          /* resolved S */
   int32_t pages_per_request; /* ceil(max_context / page_size) */
+  size_t host_row_stride;    /* bytes between consecutive rows of the host store: row_bytes, or
+                                592 for fp8 (576 code bytes, the fp32 row scale at byte 576, then
+                                12 unused bytes), so that a missed row and its scale are one
+                                16-byte-aligned read of 37 chunks */
 } hs_pool_sizes;
 
 /* Byte offsets of the state arrays inside the caller's workspace, so that a
@@ -173,8 +177,9 @@ hs_status hs_pool_requirements(const hs_pool_desc* desc, hs_pool_sizes* out);
  *                physical row r = page * page_size + offset-in-page
  *   pool_scales  device fp32 [pool rows] for HS_FP8_E4M3, else NULL
  *   state        device workspace, >= state_bytes, 256-byte aligned
- * Allocates the pinned host row store (host_rows rows of row_bytes, plus
- * fp32 scales for fp8), mapped for direct device reads over PCIe, and
+ * Allocates the pinned host row store (host_rows rows of host_row_stride
+ * bytes; an fp8 row carries its fp32 scale), mapped for direct device reads
+ * over PCIe, and
  * enqueues the state initialisation on `stream` (every page host-only, every
  * hot buffer empty, counters and the error word zero). *out receives the
  * handle. Errors: those of hs_pool_requirements, INVALID_ARGUMENT (null or
@@ -183,8 +188,10 @@ hs_status hs_init_pool(const hs_pool_desc* desc, void* pool_rows, float* pool_sc
                        void* state, size_t state_bytes, hipStream_t stream, hs_pool** out);
 
 /* Pinned host store of the pool ([P2] §"混合 HiSparse 的技术实现", state 2:
- * misses are copied from pinned host memory). *rows: host_rows x row_bytes,
- * row-major; *scales: fp32 [host_rows] for fp8 pools, else NULL. The caller
+ * misses are copied from pinned host memory). *rows: host_rows rows, row r
+ * at byte r * host_row_stride, its first row_bytes bytes the row; *scales:
+ * for fp8 pools the fp32 scale of row 0 (row r's at byte r * host_row_stride
+ * of *scales), else NULL. The caller
  * fills it (the store keeps a copy of every row, so any page can be
  * demoted at any time). Errors: INVALID_ARGUMENT. */
 hs_status hs_host_rows(hs_pool* pool, void** rows, float** scales);

@@ -40,7 +40,7 @@ class HsPoolSizes(ctypes.Structure):
     _fields_ = [("row_bytes", ctypes.c_size_t), ("pool_bytes", ctypes.c_size_t),
                 ("pool_scale_bytes", ctypes.c_size_t), ("state_bytes", ctypes.c_size_t),
                 ("host_store_bytes", ctypes.c_size_t), ("hot_rows", ctypes.c_int32),
-                ("pages_per_request", ctypes.c_int32)]
+                ("pages_per_request", ctypes.c_int32), ("host_row_stride", ctypes.c_size_t)]
 
 
 class HsStateLayout(ctypes.Structure):

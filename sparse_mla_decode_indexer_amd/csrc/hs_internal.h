@@ -14,6 +14,7 @@ constexpr int kRowDim = 576;       // 512 nope + 64 rope
 constexpr int kNope = 512;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxHotRows = 8192;
+constexpr int kHostRowStrideFp8 = 592;  // fp8 host row: 576 code bytes, fp32 scale, 12 unused bytes
 
 // top-K: one filter workgroup scans one chunk of kTkChunk scores
 constexpr int kTkChunk = 2048;
@@ -69,7 +70,7 @@ struct hs_pool {
   uint8_t* state;             // device workspace
   uint8_t* static_scratch;    // device address of this device's no-alloc scratch array
   void* host_rows;            // pinned, mapped
-  float* host_scales;         // pinned, mapped (fp8) or null
+  float* host_scales;         // fp8: the scale of host row 0 (row r's at byte r * host_row_stride), or null
 };
 
 namespace hs {

@@ -59,8 +59,10 @@ static hs_status plan_layout(const hs_pool_desc* d, hs_pool_sizes* sz, hs_state_
   sz->pool_scale_bytes = d->kv_dtype == HS_FP8_E4M3 ? 4 * (size_t)pool_rows : 0;
   sz->hot_rows = S;
   sz->pages_per_request = ppr;
-  sz->host_store_bytes = rb * (size_t)d->host_rows +
-                         (d->kv_dtype == HS_FP8_E4M3 ? 4 * (size_t)d->host_rows : 0);
+  // an fp8 host row carries its fp32 scale after the 576 code bytes (one
+  // read per miss), padded to a multiple of 16 bytes
+  sz->host_row_stride = d->kv_dtype == HS_FP8_E4M3 ? kHostRowStrideFp8 : rb;
+  sz->host_store_bytes = sz->host_row_stride * (size_t)d->host_rows;
 
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -286,7 +288,7 @@ hs_status hs_init_pool(const hs_pool_desc* desc, void* pool_rows, float* pool_sc
   }
   p->host_rows = h;
   p->host_scales = desc->kv_dtype == HS_FP8_E4M3
-                       ? reinterpret_cast<float*>(static_cast<uint8_t*>(h) + sz.row_bytes * (size_t)desc->host_rows)
+                       ? reinterpret_cast<float*>(static_cast<uint8_t*>(h) + kRowDim)
                        : nullptr;
 
   // State initialisation: everything zero, then the -1 tables and the

@@ -42,8 +42,8 @@ struct RuArgs {
   const uint8_t* pool_rows;
   const float* pool_scales;
   uint8_t* host_rows;
-  float* host_scales;
   int row_bytes;
+  int host_stride;  // bytes between host rows (fp8: the row's scale follows its codes)
   int32_t* freed_out;   // [n_req][max_demote] or null
   int32_t* counts_out;  // [n_req][2] or null
   int32_t* list;        // [n_req][kRuMaxList][2] pages to copy: (logical page, pool page)
@@ -227,7 +227,8 @@ __global__ __launch_bounds__(kRuThreads) void k_update_residency(RuArgs a, State
 
 // Copy of the listed pages into the host store: request blockIdx.y, the
 // grid's x workgroups stride over its pages 64 bytes per thread, then over
-// its fp8 scales. Writes go over PCIe into the mapped pinned store.
+// its fp8 scales (each written after its row's codes). Writes go over PCIe
+// into the mapped pinned store.
 __global__ __launch_bounds__(256) void k_residency_copy(RuArgs a, StateView v) {
   const int i = blockIdx.y;
   const int r = a.req_ids[i];
@@ -239,23 +240,26 @@ __global__ __launch_bounds__(256) void k_residency_copy(RuArgs a, StateView v) {
   const int64_t hbase = v.host_base[r];
   const int32_t* lst = a.list + (size_t)i * kRuMaxList * 2;
   const int stride = gridDim.x * 256;
-  // 4 consecutive 16-byte chunks of one page per thread (a page is a
-  // multiple of 4 chunks: 64 B per lane in flight, 4 KiB per wave)
+  // 4 consecutive 16-byte chunks of one row per thread (a row is a multiple
+  // of 4 chunks: 64 B per lane in flight, 4 KiB per wave)
   for (int x = (blockIdx.x * 256 + threadIdx.x) * 4; x < n * per_page; x += stride * 4) {
     const int k = x / per_page, rem = x - k * per_page;
+    const int row = rem / CH, c = rem - row * CH;
     const int lp = lst[2 * k], gp = lst[2 * k + 1];
     const ru_u32x4* src = reinterpret_cast<const ru_u32x4*>(a.pool_rows + (int64_t)gp * ps * a.row_bytes) + rem;
-    ru_u32x4* dst = reinterpret_cast<ru_u32x4*>(a.host_rows + (hbase + (int64_t)lp * ps) * a.row_bytes) + rem;
+    ru_u32x4* dst =
+        reinterpret_cast<ru_u32x4*>(a.host_rows + (hbase + (int64_t)lp * ps + row) * a.host_stride) + c;
     const ru_u32x4 t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
     dst[0] = t0;
     dst[1] = t1;
     dst[2] = t2;
     dst[3] = t3;
   }
-  if (a.host_scales)
+  if (a.pool_scales)
     for (int x = blockIdx.x * 256 + threadIdx.x; x < n * ps; x += stride) {
       const int k = x >> lps, o = x & (ps - 1);
-      a.host_scales[hbase + (int64_t)lst[2 * k] * ps + o] = a.pool_scales[(int64_t)lst[2 * k + 1] * ps + o];
+      *reinterpret_cast<float*>(a.host_rows + (hbase + (int64_t)lst[2 * k] * ps + o) * a.host_stride + a.row_bytes) =
+          a.pool_scales[(int64_t)lst[2 * k + 1] * ps + o];
     }
 }
 
@@ -270,8 +274,8 @@ hs_status launch_update_residency(hs_pool* p, const int32_t* req_ids, int32_t n_
   a.pool_rows = p->pool_rows;
   a.pool_scales = p->pool_scales;
   a.host_rows = static_cast<uint8_t*>(p->host_rows);
-  a.host_scales = p->host_scales;
   a.row_bytes = (int)p->sz.row_bytes;
+  a.host_stride = (int)p->sz.host_row_stride;
   a.freed_out = freed_out;
   a.counts_out = counts_out;
   a.list = reinterpret_cast<int32_t*>(p->state + p->off.ru_list);

@@ -108,8 +108,7 @@ struct RsArgs {
   int spin_limit;  // polls of a destination before a copy wave gives up
   int32_t* plan_out;
   int32_t* counts_out;
-  const uint8_t* host_rows;
-  const float* host_scales;
+  const uint8_t* host_rows;  // fp8 rows carry their scale (host row stride kHostRowStrideFp8)
   uint8_t* pool_rows;
   float* pool_scales;
   // select-and-resolve only: the scores, the top-K scratch and the LDS
@@ -533,8 +532,11 @@ __device__ __forceinline__ void bookkeep(const RsArgs& a, const StateView& v, co
 template <int ROW_BYTES, bool FP8, bool FUSED>
 __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc,
                                           int i, int c, uint32_t epoch) {
-  constexpr int CH = ROW_BYTES / 16;   // 16-byte chunks per row
-  constexpr int CPL = (CH + 63) / 64;  // chunks per lane
+  constexpr int CH = ROW_BYTES / 16;        // 16-byte chunks of a pool row
+  constexpr int HCH = FP8 ? CH + 1 : CH;    // ... of a host row (fp8: then the chunk holding the scale)
+  constexpr int HSTRIDE = 16 * HCH;         // host row stride
+  static_assert(!FP8 || HSTRIDE == kHostRowStrideFp8, "fp8 host rows carry their scale");
+  constexpr int CPL = (HCH + 63) / 64;      // chunks per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = v.top_k, lps = v.log2_ps;
   const int j0 = kRsPart * c + 4 * wave;
@@ -587,15 +589,12 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if ((gb >> k) & 1u) {
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * ROW_BYTES);
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * HSTRIDE);
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) x[k][u] = s4[lane + 64 * u];
+        if (lane + 64 * u < HCH) x[k][u] = s4[lane + 64 * u];  // (fp8: the scale comes with the row)
     }
   }
-  // the fp8 scale of a guessed miss is read with its row (lane k: position k)
-  float scale = 0.f;
-  if (FP8 && guess) scale = a.host_scales[hbase + t];
   // wait for the bookkeeper (each wave on its own): lanes 0..3 poll their
   // positions' destinations with device-coherent loads until each carries
   // this launch's epoch
@@ -640,23 +639,24 @@ __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, c
     const int dst = dsts[k];
     if (dst < 0) continue;
     u32x4* d4 = reinterpret_cast<u32x4*>(a.pool_rows + (int64_t)dst * ROW_BYTES);
+    u32x4 y[CPL];
     if ((gb >> k) & 1u) {
 #pragma unroll
-      for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) __builtin_nontemporal_store(x[k][u], d4 + lane + 64 * u);  // (streaming)
+      for (int u = 0; u < CPL; ++u) y[u] = x[k][u];
     } else {  // a miss that was not guessed (rare): read it now
-      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * ROW_BYTES);
-      u32x4 y[CPL];
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.host_rows + (hbase + tk[k]) * HSTRIDE);
 #pragma unroll
       for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) y[u] = s4[lane + 64 * u];
+        if (lane + 64 * u < HCH) y[u] = s4[lane + 64 * u];
+    }
 #pragma unroll
-      for (int u = 0; u < CPL; ++u)
-        if (lane + 64 * u < CH) __builtin_nontemporal_store(y[u], d4 + lane + 64 * u);
+    for (int u = 0; u < CPL; ++u)
+      if (lane + 64 * u < CH) __builtin_nontemporal_store(y[u], d4 + lane + 64 * u);  // (streaming)
+    if constexpr (FP8) {  // the row's scale: first word of host chunk CH
+      const uint32_t sbits = (uint32_t)__shfl((int)y[CH / 64][0], CH % 64, 64);
+      if (lane == k) a.pool_scales[dst] = __uint_as_float(sbits);
     }
   }
-  if (FP8 && lane < 4 && md >= 0)  // one scale per missed row (read now if not guessed)
-    a.pool_scales[md] = guess ? scale : a.host_scales[hbase + t];
   // LRU tables of every miss: the slot's old token leaves the reverse map,
   // the missed token takes the slot (a missed token is in no slot, so it is
   // never another miss's old token: these stores do not collide)
@@ -754,7 +754,7 @@ static hs_status launch_resolve_impl(hs_pool* p, const int32_t* idx, const int32
            max(4, pow2_at_least((v.hot_rows + kRsThreads - 1) / kRsThreads)),
            v.pages_per_req <= kRsPtLds ? v.pages_per_req : 0, spin_limit(),
            plan_out, counts_out, static_cast<const uint8_t*>(p->host_rows),
-           p->host_scales, p->pool_rows, p->pool_scales, scores, score_stride, make_tk_scratch(p, 1), 0};
+           p->pool_rows, p->pool_scales, scores, score_stride, make_tk_scratch(p, 1), 0};
   size_t dyn = (rs_dyn_bytes(a.Q * kRsThreads, p->d.top_k, v.hot_pages_per_req, a.pt_lds) + 15) & ~(size_t)15;
   if (FUSED) {  // the select's LDS (the bookkeeping reuses it), then the selection
     if (dyn < kTkSelLdsBytes) dyn = kTkSelLdsBytes;

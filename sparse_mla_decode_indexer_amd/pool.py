@@ -47,11 +47,15 @@ class TieredPool:
         assert self.state.data_ptr() % 256 == 0
         self.handle = B.init_pool(self.desc, self.pool_rows.data_ptr(), _ptr(self.pool_scales),
                                   self.state.data_ptr(), int(self.sizes.state_bytes), _stream())
+        # host store views: row r at byte r * host_row_stride; an fp8 row's
+        # fp32 scale follows its 576 code bytes
         rows_p, scales_p = B.host_rows(self.handle)
-        n = host_rows * self.row_bytes
-        self.host_store = np.ctypeslib.as_array((ctypes.c_uint8 * n).from_address(rows_p)).reshape(
-            host_rows, self.row_bytes)
-        self.host_scales = (np.ctypeslib.as_array((ctypes.c_float * host_rows).from_address(scales_p))
+        stride = int(self.sizes.host_row_stride)
+        raw = (ctypes.c_uint8 * (host_rows * stride)).from_address(rows_p)
+        self.host_store = np.ndarray((host_rows, self.row_bytes), dtype=np.uint8, buffer=raw,
+                                     strides=(stride, 1))
+        self.host_scales = (np.ndarray((host_rows,), dtype=np.float32, buffer=raw,
+                                       offset=scales_p - rows_p, strides=(stride,))
                             if kv_dtype == "fp8" else None)
         self.layout = B.get_state_layout(self.handle)
         self.hot_rows = int(self.sizes.hot_rows)

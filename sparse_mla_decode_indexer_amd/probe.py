@@ -7,7 +7,8 @@ kernels run on:
   * PCIe host read: zero-copy coalesced reads of a 512 MiB pinned, mapped
     host buffer (the kind of memory the pool's host store is), best of a
     few grid sizes; and whole-row reads of random 1,152-byte (bf16) and
-    580-byte-class (576-byte fp8 payload) rows, the miss copy's pattern;
+    592-byte rows (576 fp8 code bytes and the row scale, padded to 16-byte
+    chunks, as the host store holds them), the miss copy's pattern;
   * HBM: a plain device copy (bytes read + written) and a plain device read;
   * MFMA: independent chains of the bf16 16x16x32 MFMA the attention kernel
     uses, counted at 16,384 FLOP each.
@@ -102,7 +103,7 @@ def measure(host_mib: int = 512, copy_mib: int = 1024, reps: int = 5) -> dict:
         out["pcie_host_read"] = {"bytes": nbytes, "gbs_by_grid": grids, "kind": "zero-copy coalesced 16-B loads"}
         rng = np.random.default_rng(1)
         gathers = {}
-        for rb in (1152, 576):
+        for rb in (1152, 592):
             n_src = nbytes // rb
             n = 65536
             rows = torch.from_numpy(rng.integers(0, n_src, size=n).astype(np.int64)).cuda()

@@ -36,10 +36,11 @@ def test_requirements_sizes():
     s = B.pool_requirements(desc())
     assert s.row_bytes == 1152 and s.hot_rows == 4096 and s.pages_per_request == 128
     assert s.pool_bytes == 128 * 64 * 1152 and s.pool_scale_bytes == 0
-    assert s.host_store_bytes == 16384 * 1152
+    assert s.host_store_bytes == 16384 * 1152 and s.host_row_stride == 1152
     f8 = B.pool_requirements(desc(kv_dtype=B.HS_FP8_E4M3))
     assert f8.row_bytes == 576 and f8.pool_scale_bytes == 4 * 128 * 64
-    assert f8.host_store_bytes == 16384 * 580
+    # an fp8 host row carries its scale: 576 code bytes + 4 + 12 unused
+    assert f8.host_row_stride == 592 and f8.host_store_bytes == 16384 * 592
     assert B.pool_requirements(desc(kv_dtype=B.HS_F32)).row_bytes == 2304
 
 
