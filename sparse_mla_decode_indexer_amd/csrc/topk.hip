@@ -234,9 +234,79 @@ __global__ __launch_bounds__(kUnThreads) void k_topk_union(const int32_t* __rest
   for (int x = base + tid; x < cap; x += kUnThreads) uo[x] = -1;
 }
 
+// The same union through a bitmap of the token space (pools whose
+// max_context fits it in LDS): every valid entry sets its token's bit; the
+// union position of token x is the number of set bits below x, from an
+// exclusive prefix of the words' popcounts (16 bits each: a union holds at
+// most kMaxTopK tokens); each thread emits the set bits of its own run of
+// words at their positions, so the union comes out ascending. No search,
+// three barriers.
+constexpr size_t kUnBitmapMaxLds = (size_t)150 << 10;
+__host__ __device__ inline size_t union_bitmap_lds(int words) { return 4 * (size_t)words + 2 * (size_t)((words + 1) & ~1); }
+
+__global__ __launch_bounds__(kUnThreads) void k_topk_union_bitmap(const int32_t* __restrict__ idx, int qsel, int K,
+                                                                  int cap, int words, int32_t* __restrict__ union_out,
+                                                                  int32_t* __restrict__ upos_out) {
+  extern __shared__ __align__(16) uint32_t un_dyn[];
+  uint32_t* bm = un_dyn;                                  // [words]
+  uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + words);  // [words] set bits in the words before
+  __shared__ int wtot[kUnThreads / 64 + 1];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int n = qsel * K;  // <= cap <= kMaxTopK
+  const int32_t* src = idx + (size_t)i * n;
+  for (int w = tid; w < words; w += kUnThreads) bm[w] = 0u;
+  int tok[kUnRounds];
+#pragma unroll
+  for (int e = 0; e < kUnRounds; ++e) {
+    const int x = e * kUnThreads + tid;
+    const int t = x < n ? src[x] : -1;
+    tok[e] = (t >= 0 && t < 32 * words) ? t : -1;  // (padding is -1; every selected token is below max_context)
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kUnRounds; ++e)
+    if (tok[e] >= 0) atomicOr(&bm[tok[e] >> 5], 1u << (tok[e] & 31));
+  __syncthreads();
+  // this thread's run of words [w0, w1)
+  const int per = (words + kUnThreads - 1) / kUnThreads;
+  const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  int total;
+  int run = block_excl_sum(cnt, wtot, total);
+  for (int w = w0; w < w1; ++w) {
+    wpre[w] = (uint16_t)run;
+    run += __popc(bm[w]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kUnRounds; ++e) {
+    const int x = e * kUnThreads + tid;
+    if (x < n) {
+      const int t = tok[e];
+      upos_out[(size_t)i * n + x] = t >= 0 ? (int)wpre[t >> 5] + __popc(bm[t >> 5] & ((1u << (t & 31)) - 1u)) : -1;
+    }
+  }
+  int32_t* uo = union_out + (size_t)i * cap;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = bm[w];
+    int p = wpre[w];
+    while (b) {
+      uo[p++] = 32 * w + __builtin_ctz(b);
+      b &= b - 1u;
+    }
+  }
+  for (int x = total + tid; x < cap; x += kUnThreads) uo[x] = -1;
+}
+
 hs_status launch_topk_union(hs_pool* p, const int32_t* idx, int32_t n_req, int32_t qsel, int32_t k,
                             int32_t* union_out, int32_t* upos_out, hipStream_t s) {
-  k_topk_union<<<n_req, kUnThreads, 0, s>>>(idx, qsel, k, p->d.top_k, union_out, upos_out);
+  const int words = (p->d.max_context + 31) / 32;
+  const size_t lds = union_bitmap_lds(words);
+  if (lds <= kUnBitmapMaxLds)
+    k_topk_union_bitmap<<<n_req, kUnThreads, lds, s>>>(idx, qsel, k, p->d.top_k, words, union_out, upos_out);
+  else  // (contexts beyond ~800K tokens: the search form)
+    k_topk_union<<<n_req, kUnThreads, 0, s>>>(idx, qsel, k, p->d.top_k, union_out, upos_out);
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
 }
