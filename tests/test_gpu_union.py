@@ -171,3 +171,46 @@ def test_select_resolve_step_graph_replays_match_two_calls():
     _graph_vs_eager(small("batch32", n_req=5, ctx_range=(4096, 40000), steps=4),
                     lambda pool, buf: Hn.decode_step(pool, buf, 0, fused=True),
                     eager_fn=lambda pool, buf: Hn.decode_step(pool, buf, 0))
+
+
+@pytest.mark.parametrize("max_ctx", [20000, 1 << 20], ids=["bitmap", "search"])
+def test_union_kernel_forms(max_ctx):
+    """The union of per-token selections is formed from a token bitmap in LDS
+    when the pool's max_context fits one, else by binary searches over the
+    selections (here: a pool sized for 1M-token contexts). Either way it
+    equals the per-token definition: each query token's top-k of its own
+    scores, their sorted union and each selected token's union position."""
+    from oracle import select_topk, union_of_selections
+    from sparse_mla_decode_indexer_amd.pool import TieredPool
+    log(f"[gpu] union kernel form for max_context {max_ctx}")
+    Q, k, cap, R = 4, 512, 2048, 3
+    lens = [300, 9000, 20000]  # L < k, L > k, L = the small pool's max_context
+    rng = np.random.default_rng(11)
+    pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=R, max_context=max_ctx, kv_dtype="bf16",
+                      top_k=cap, hot_rows=cap, max_batch=R, max_q_rows=64, host_rows=R * 20000, select_q=Q)
+    try:
+        stride = max_ctx
+        sc = np.zeros((R, Q, stride), dtype=np.float32)
+        for r, L in enumerate(lens):
+            base = rng.standard_normal(L).astype(np.float32)
+            for t in range(Q):  # nearby drafts: overlapping but different selections
+                sc[r, t, :L] = base + np.float32(0.3) * rng.standard_normal(L).astype(np.float32)
+            sc[r, 2, :L:7] = sc[r, 1, :L:7]  # some equal scores across tokens
+            pool.set_residency(r, L, r * 20000, None)
+        d_sc = torch.from_numpy(sc).cuda()
+        req = torch.arange(R, dtype=torch.int32, device="cuda")
+        sel = torch.full((R, Q, k), -5, dtype=torch.int32, device="cuda")
+        union = torch.full((R, cap), -5, dtype=torch.int32, device="cuda")
+        upos = torch.full((R, Q, k), -5, dtype=torch.int32, device="cuda")
+        for rep in range(2):  # the scratch must be clean for a second call
+            pool.select_topk_union(d_sc, req, sel, union, upos)
+            g_sel, g_un, g_up = sel.cpu().numpy(), union.cpu().numpy(), upos.cpu().numpy()
+            for r, L in enumerate(lens):
+                want = [select_topk(sc[r, t], L, k) for t in range(Q)]
+                u_ref, up_ref = union_of_selections(want, cap)
+                assert np.array_equal(g_sel[r], np.stack(want)), (rep, r)
+                assert np.array_equal(g_un[r], u_ref), (rep, r)
+                assert np.array_equal(g_up[r], up_ref), (rep, r)
+        assert pool.device_error()[0] == 0
+    finally:
+        pool.close()
