@@ -368,7 +368,8 @@ hs_status hs_sparse_mla_decode(hs_pool* pool, const void* q, int32_t q_dtype,
  * allocating library routine). A batch whose smallest split needs more than
  * 8,176 partial rows (n_req * q_per_req * n_heads * ceil(top_k / 2048) with
  * top_k > 2048; with top_k <= 2048 no partials are needed) returns
- * HS_ERR_CAPACITY and enqueues nothing. Every call on one GPU shares that
+ * HS_ERR_CAPACITY and enqueues nothing (fp32 pools split their plans only
+ * as far as the array holds, so they never get this error). Every call on one GPU shares that
  * GPU's array, so calls whose kernels overlap on one GPU (other streams,
  * other pools, other threads) race; calls on one stream do not. The array
  * needs no clearing: every partial a call reads was written by that call.

@@ -52,6 +52,7 @@
 // units, one workgroup per query row.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include <math.h>
@@ -640,18 +641,23 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(int n_rows, in
   if (lse_out && d4 == 0) lse_out[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 
-// fp32 rows and queries: one workgroup per query row, fp32 on the vector
-// units. Scores: wave w takes rows w, w + 4, ...; the 64 lanes read a row's
-// 576 values together (9 each, coalesced), 16 rows in flight per wave,
-// and sum across lanes. Weighted sum: thread t owns output dims t and
-// t + 256 and walks the rows in plan order, 32 rows' loads in flight;
-// absent rows read the zero row.
+// fp32 rows and queries: one workgroup per (query row, split of the plan),
+// fp32 on the vector units. Scores: wave w takes rows w, w + 4, ... of the
+// split; the 64 lanes read a row's 576 values together (9 each,
+// coalesced), 16 rows in flight per wave, and sum across lanes. Weighted
+// sum: thread t owns output dims t and t + 256 and walks the split's rows
+// in plan order, 32 rows' loads in flight; absent rows read the zero row.
+// With more than one split each writes its normalised partial output and
+// base-2 log-sum-exp for k_attn_combine.
 constexpr int kF32Threads = 256;
+constexpr int kF32MinRowsPerSplit = 32;
 __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restrict__ q, int QR,
                                                          PlanRef plan,
                                                          const float* __restrict__ pool, int64_t pool_rows_n,
                                                          const float* __restrict__ zero_row, float sm_scale,
+                                                         int rows_per_split, int n_splits,
                                                          float* __restrict__ out, float* __restrict__ lse_out,
+                                                         float* __restrict__ part_o, float* __restrict__ part_lse,
                                                          uint32_t* __restrict__ err) {
   constexpr int kPerLane = kRowDim / 64;  // 9
   constexpr int kWaves = kF32Threads / 64;
@@ -659,14 +665,15 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   __shared__ float pb[kMaxTopK];
   __shared__ int pr_s[kMaxTopK];
   __shared__ float red[kWaves];
-  const int K = plan.K;
-  const int qh = blockIdx.x, i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qh = blockIdx.x, i = blockIdx.y, sp = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j_begin = sp * rows_per_split;
+  const int K = max(0, min(plan.K, j_begin + rows_per_split) - j_begin);  // this split's rows
   const float* qr = q + ((size_t)i * QR + qh) * kRowDim;
   for (int d = tid; d < kRowDim; d += kF32Threads) qs[d] = qr[d];
   for (int j = tid; j < K; j += kF32Threads) {
-    int pr = plan_entry(plan, i, j, err);
+    int pr = plan_entry(plan, i, j_begin + j, err);
     if (pr >= pool_rows_n) {
-      raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)j);
+      raise_error(err, HS_DEV_PLAN_RANGE, (uint32_t)i, (uint32_t)(j_begin + j));
       pr = -1;
     }
     pr_s[j] = pr;
@@ -741,10 +748,18 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
       a1 += p * v1[u];
     }
   }
-  float* dst = out + ((size_t)i * QR + qh) * kNope;
-  dst[tid] = l > 0.f ? a0 / l : 0.f;
-  dst[tid + kF32Threads] = l > 0.f ? a1 / l : 0.f;
-  if (lse_out && tid == 0) lse_out[(size_t)i * QR + qh] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (n_splits == 1) {
+    float* dst = out + ((size_t)i * QR + qh) * kNope;
+    dst[tid] = l > 0.f ? a0 / l : 0.f;
+    dst[tid + kF32Threads] = l > 0.f ? a1 / l : 0.f;
+    if (lse_out && tid == 0) lse_out[(size_t)i * QR + qh] = l > 0.f ? m + logf(l) : -INFINITY;
+  } else {  // partials as the merge kernel takes them (log-sum-exp in base 2)
+    const size_t prow = ((size_t)i * n_splits + sp) * QR + qh;
+    float* dst = part_o + prow * kNope;
+    dst[tid] = l > 0.f ? a0 / l : 0.f;
+    dst[tid + kF32Threads] = l > 0.f ? a1 / l : 0.f;
+    if (tid == 0) part_lse[prow] = l > 0.f ? (m + logf(l)) * kLog2e : -INFINITY;
+  }
 }
 
 // Split partials of hs_sparse_mla_decode_noalloc (kStaticScratchBytes per
@@ -773,6 +788,25 @@ static int env_int(const char* name, int dflt) {
   return s ? atoi(s) : dflt;
 }
 
+// The merge of n_splits partials for each of `rows` query rows.
+static void launch_combine(int rows, int QR, int n_splits, const float* part_o, const float* part_lse, float* out,
+                           float* lse_out, hipStream_t s) {
+  const int64_t threads = (int64_t)rows * (kNope / 4);
+  const int nb = (int)((threads + kCombineThreads - 1) / kCombineThreads);
+#define HS_COMBINE(B) k_attn_combine<B><<<nb, kCombineThreads, 0, s>>>(rows, QR, n_splits, part_o, part_lse, out, lse_out)
+  if (n_splits <= 2)
+    HS_COMBINE(2);
+  else if (n_splits <= 4)
+    HS_COMBINE(4);
+  else if (n_splits <= 8)
+    HS_COMBINE(8);
+  else if (n_splits <= 16)
+    HS_COMBINE(16);
+  else
+    HS_COMBINE(32);
+#undef HS_COMBINE
+}
+
 hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n_req,
                            int32_t q_per_req, int32_t n_heads, const int32_t* plan, const int32_t* upos,
                            int32_t k_plan, int32_t plan_div, float sm_scale, float* out, float* lse_out,
@@ -783,9 +817,17 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   const int QR = q_per_req * n_heads;
   uint32_t* err = reinterpret_cast<uint32_t*>(p->state + p->lay.error);
   if (p->d.kv_dtype == HS_F32) {
-    k_attn_f32<<<dim3(QR, n_req), kF32Threads, 0, s>>>(
+    // splits of at least kF32MinRowsPerSplit rows, enough for ~512
+    // workgroups, within the partial rows
+    int splits = (int)std::min<int64_t>((K + kF32MinRowsPerSplit - 1) / kF32MinRowsPerSplit,
+                                        std::max<int64_t>(1, 512 / std::max<int64_t>(1, (int64_t)n_req * QR)));
+    splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, part_rows / std::max<int64_t>(1, (int64_t)n_req * QR)));
+    const int rps = (K + splits - 1) / splits;
+    k_attn_f32<<<dim3(QR, n_req, splits), kF32Threads, 0, s>>>(
         static_cast<const float*>(q), QR, pref, reinterpret_cast<const float*>(p->pool_rows), p->pool_rows_n,
-        reinterpret_cast<const float*>(p->state + p->off.zero_row), sm_scale, out, lse_out, err);
+        reinterpret_cast<const float*>(p->state + p->off.zero_row), sm_scale, rps, splits, out, lse_out, part_o,
+        part_lse, err);
+    if (splits > 1) launch_combine(n_req * QR, QR, splits, part_o, part_lse, out, lse_out, s);
     HS_HIP_CHECK(hipGetLastError());
     return HS_OK;
   }
@@ -850,23 +892,7 @@ hs_status launch_attention(hs_pool* p, const void* q, int32_t q_dtype, int32_t n
   }
 #undef HS_ATTN_LAUNCH_QB
 #undef HS_ATTN_LAUNCH
-  if (splits > 1) {
-    const int rows = n_req * QR;
-    const int64_t threads = (int64_t)rows * (kNope / 4);
-    const int nb = (int)((threads + kCombineThreads - 1) / kCombineThreads);
-#define HS_COMBINE(B) k_attn_combine<B><<<nb, kCombineThreads, 0, s>>>(rows, QR, splits, part_o, part_lse, out, lse_out)
-    if (splits <= 2)
-      HS_COMBINE(2);
-    else if (splits <= 4)
-      HS_COMBINE(4);
-    else if (splits <= 8)
-      HS_COMBINE(8);
-    else if (splits <= 16)
-      HS_COMBINE(16);
-    else
-      HS_COMBINE(32);
-#undef HS_COMBINE
-  }
+  if (splits > 1) launch_combine(n_req * QR, QR, splits, part_o, part_lse, out, lse_out, s);
   HS_HIP_CHECK(hipGetLastError());
   return HS_OK;
 }
