@@ -340,6 +340,15 @@ __device__ __forceinline__ void select_row(const float* __restrict__ scores, int
       }
     }
   } else if (staged && !narrowed) {
+    // The chunk of every survivor from a table that one lane per chunk
+    // fills (in the third histogram, unused until the lower digits and
+    // cleared again below: n <= kTkStage entries of 16 bits), instead of a
+    // binary search over the chunk offsets per survivor.
+    static_assert(kTkStage * 2 <= kTkBins * 4 && kTkMaxChunks <= 65536, "chunk table fits a histogram");
+    uint16_t* owner = reinterpret_cast<uint16_t*>(hist[2]);
+    for (int c = tid; c < nch; c += kTkSelThreads)
+      for (int x = off[c]; x < off[c + 1]; ++x) owner[x] = (uint16_t)c;
+    __syncthreads();
     constexpr int U = 4;
     for (int x0 = tid; x0 < n; x0 += U * kTkSelThreads) {
       uint2 e[U];
@@ -347,12 +356,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ scores, int
       for (int u = 0; u < U; ++u) {
         const int x = x0 + u * kTkSelThreads;
         if (x < n) {
-          int lo = 0, hi = nch;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (off[mid] <= x) lo = mid; else hi = mid;
-          }
-          e[u] = cand[(size_t)lo * kTkChunk + (x - off[lo])];
+          const int c = owner[x];
+          e[u] = cand[(size_t)c * kTkChunk + (x - off[c])];
         }
       }
 #pragma unroll
@@ -364,6 +369,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ scores, int
         }
       }
     }
+    __syncthreads();  // every owner entry has been read
+    for (int b = tid; b < kTkBins; b += kTkSelThreads) hist[2][b] = 0u;
   } else {
     for (int x = tid; x < n; x += kTkSelThreads) atomicAdd(&hist[0][(get(x).x - base) >> s1], 1u);
   }
