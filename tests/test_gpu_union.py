@@ -173,17 +173,20 @@ def test_select_resolve_step_graph_replays_match_two_calls():
                     eager_fn=lambda pool, buf: Hn.decode_step(pool, buf, 0))
 
 
+@pytest.mark.parametrize("Q,cap", [(4, 2048), (8, 4096)], ids=["q4", "q8-limits"])
 @pytest.mark.parametrize("max_ctx", [20000, 1 << 20], ids=["bitmap", "search"])
-def test_union_kernel_forms(max_ctx):
+def test_union_kernel_forms(max_ctx, Q, cap):
     """The union of per-token selections is formed from a token bitmap in LDS
     when the pool's max_context fits one, else by binary searches over the
     selections (here: a pool sized for 1M-token contexts). Either way it
     equals the per-token definition: each query token's top-k of its own
-    scores, their sorted union and each selected token's union position."""
+    scores, their sorted union and each selected token's union position.
+    Also at the limits: 8 query tokens with a selection each (the most)
+    and a union capacity of 4,096 (the largest top-K)."""
     from oracle import select_topk, union_of_selections
     from sparse_mla_decode_indexer_amd.pool import TieredPool
-    log(f"[gpu] union kernel form for max_context {max_ctx}")
-    Q, k, cap, R = 4, 512, 2048, 3
+    log(f"[gpu] union kernel form for max_context {max_ctx}, Q={Q}, capacity {cap}")
+    k, R = 512, 3
     lens = [300, 9000, 20000]  # L < k, L > k, L = the small pool's max_context
     rng = np.random.default_rng(11)
     pool = TieredPool(page_size=64, num_pool_pages=8, max_requests=R, max_context=max_ctx, kv_dtype="bf16",
@@ -196,6 +199,8 @@ def test_union_kernel_forms(max_ctx):
             for t in range(Q):  # nearby drafts: overlapping but different selections
                 sc[r, t, :L] = base + np.float32(0.3) * rng.standard_normal(L).astype(np.float32)
             sc[r, 2, :L:7] = sc[r, 1, :L:7]  # some equal scores across tokens
+            if Q > 4:  # independent drafts: unions near the capacity
+                sc[r, 4:, :L] = rng.standard_normal((Q - 4, L)).astype(np.float32)
             pool.set_residency(r, L, r * 20000, None)
         d_sc = torch.from_numpy(sc).cuda()
         req = torch.arange(R, dtype=torch.int32, device="cuda")
