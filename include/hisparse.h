@@ -115,7 +115,8 @@ typedef struct hs_pool_desc {
   int32_t page_size;      /* tokens per page: power of two in [1, 1024] */
   int32_t num_pool_pages; /* device pool pages (resident pages + leased hot pages) */
   int32_t max_requests;   /* request ids are 0 .. max_requests-1 */
-  int32_t max_context;    /* most tokens any request holds, >= 1 */
+  int32_t max_context;    /* most tokens any request holds: 1 .. 4,194,304 (the top-K
+                             filter's 2,048 chunks of 2,048 scores) */
   int32_t nope_dim;       /* must be 512 */
   int32_t rope_dim;       /* must be 64 */
   int32_t kv_dtype;       /* hs_dtype of the stored rows */
@@ -169,7 +170,8 @@ typedef struct hs_state_layout {
 
 /* Derive buffer sizes from a descriptor. Pure host computation.
  * Errors: INVALID_ARGUMENT (null or malformed descriptor), CAPACITY
- * (hot_rows < top_k), UNSUPPORTED (dims other than 512 + 64). */
+ * (hot_rows < top_k or > 8192, max_context > 4,194,304, more than 2^31 - 1
+ * pool rows), UNSUPPORTED (dims other than 512 + 64, unknown kv_dtype). */
 hs_status hs_pool_requirements(const hs_pool_desc* desc, hs_pool_sizes* out);
 
 /* Create a pool over caller-owned device memory.

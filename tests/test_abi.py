@@ -44,6 +44,13 @@ def test_requirements_sizes():
     assert B.pool_requirements(desc(kv_dtype=B.HS_F32)).row_bytes == 2304
 
 
+def test_requirements_at_the_limits():
+    _lib()
+    s = B.pool_requirements(desc(max_context=4194304, top_k=4096, hot_rows=8192, select_q=8,
+                                 kv_dtype=B.HS_FP8_E4M3))
+    assert s.pages_per_request == 65536 and s.hot_rows == 8192
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(hot_rows=1024), 2),          # S < K
     (dict(hot_rows=4100), 1),          # not a page multiple
@@ -54,6 +61,10 @@ def test_requirements_sizes():
     (dict(max_batch=3), 1),
     (dict(select_q=9), 1),
     (dict(select_q=-1), 1),
+    (dict(top_k=4097, hot_rows=8192), 1),            # K above the largest top-K
+    (dict(hot_rows=8256), 2),                       # above the largest hot buffer
+    (dict(max_context=4194305), 2),                 # more than 2,048 filter chunks
+    (dict(num_pool_pages=1 << 25, page_size=64), 2),  # more than 2^31 - 1 pool rows
 ])
 def test_requirements_rejects(kw, status):
     _lib()
