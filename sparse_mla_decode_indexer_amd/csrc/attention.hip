@@ -12,10 +12,11 @@
 // takes 64 query rows (4 blocks of 16; or 4 waves and 32 rows when only a
 // few requests are decoded) of one request and a contiguous split of its
 // plan, 32 rows (a tile) at a time:
-//   - rows are fetched straight from the pool into LDS (global_load_lds,
-//     no registers), through a ring of three buffers: tiles t+1 and t+2
-//     are in flight while tile t is computed, and the queries load under
-//     the first gathers; fp8 codes land raw and are widened to bf16 in LDS (exact);
+//   - rows are fetched straight from the pool into LDS (buffer_load ... lds,
+//     or global_load_lds for pools over 4 GB; no registers), through a ring
+//     of three buffers: tiles t+1 and t+2 are in flight while tile t is
+//     computed, and the queries load under the first gathers; fp8 codes
+//     land raw and are widened to fp16 in LDS (exact);
 //     absent rows read zeros; rows sit 73 chunks of 16 bytes apart in
 //     LDS (one pad chunk), so the MFMA operand reads of 16 rows at one
 //     column hit distinct banks and operand addresses are a base plus an
@@ -49,7 +50,8 @@
 // log-sum-exp; k_attn_combine merges them.
 //
 // k_attn_f32 (fp32 rows and queries): plain fp32 arithmetic on the vector
-// units, one workgroup per query row.
+// units, one workgroup per (query row, split of the plan), the splits
+// merged by k_attn_combine.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
