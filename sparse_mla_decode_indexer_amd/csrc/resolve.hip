@@ -17,7 +17,9 @@
 //     wave): reads the page table and reverse map itself to guess which of
 //     its tokens miss and starts reading those rows from the mapped host
 //     store over PCIe right away; each wave then waits until its four copy
-//     destinations are published, writes the rows the bookkeeper actually
+//     destinations are published (a wave whose four positions are padding
+//     or on resident pages cannot hold a miss and ends at once), writes the
+//     rows the bookkeeper actually
 //     classified as misses into their hot slots (rows it did not guess are
 //     read then) and moves the slots' tags and reverse-map entries from the
 //     old tokens to the new. The guess only decides how early the PCIe reads
