@@ -140,9 +140,9 @@ typedef struct hs_pool_sizes {
   int32_t hot_rows;          /* resolved S */
   int32_t pages_per_request; /* ceil(max_context / page_size) */
   size_t host_row_stride;    /* bytes between consecutive rows of the host store: row_bytes, or
-                                592 for fp8 (576 code bytes, the fp32 row scale at byte 576, then
-                                12 unused bytes), so that a missed row and its scale are one
-                                16-byte-aligned read of 37 chunks */
+                                640 for fp8 (576 code bytes, the fp32 row scale at byte 576, then
+                                60 unused bytes), so that a missed row and its scale are one read
+                                of 37 16-byte chunks starting on a 128-byte boundary */
 } hs_pool_sizes;
 
 /* Byte offsets of the state arrays inside the caller's workspace, so that a

@@ -41,13 +41,15 @@ int32_t hsp_free_pinned(void* p);
  * never occurs; it keeps the loads from being dropped. */
 int32_t hsp_host_read(const void* src, size_t bytes, int32_t blocks, uint32_t* sink, hipStream_t stream);
 
-/* Zero-copy read of `n_rows` whole rows of `row_bytes` bytes (a multiple
- * of 16, at most 4096) at host row indices `rows` (device int64) of the
- * `src_rows` rows at `src`, one wave per row, written to device memory
- * `dst` (n_rows x row_bytes): the access pattern of the miss copy. An index
- * outside [0, src_rows) is skipped (its destination row is not written). */
-int32_t hsp_host_gather(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
-                        int32_t n_rows, void* dst, hipStream_t stream);
+/* Zero-copy read of `n_rows` rows of `row_bytes` bytes (a multiple of 16,
+ * at most 4096) at host row indices `rows` (device int64) of the `src_rows`
+ * rows at `src`, `row_stride` bytes apart (>= row_bytes, a multiple of 16),
+ * one wave per row, written to device memory `dst` (n_rows x row_bytes):
+ * the access pattern of the miss copy. An index outside [0, src_rows) is
+ * skipped (its destination row is not written); the caller keeps
+ * src_rows * row_stride within the buffer. */
+int32_t hsp_host_gather(const void* src, int64_t src_rows, int64_t row_bytes, int64_t row_stride,
+                        const int64_t* rows, int32_t n_rows, void* dst, hipStream_t stream);
 
 /* Device copy of `bytes` (a multiple of 16) from `src` to `dst` (both
  * device memory), 16-byte words, grid-stride over `blocks` x 256 threads. */

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src
 
 // One wave per row: the row's 16-byte words spread over the wave's lanes.
 __global__ __launch_bounds__(kThreads) void k_gather(const uint8_t* __restrict__ src, int64_t src_rows,
-                                                     int64_t row_bytes, const int64_t* __restrict__ rows,
+                                                     int64_t row_bytes, int64_t row_stride,
+                                                     const int64_t* __restrict__ rows,
                                                      int n_rows, uint8_t* __restrict__ dst) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = blockIdx.x * (kThreads / 64) + wave;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint8_t* __restrict__
   const int64_t r = rows[j];
   if (r < 0 || r >= src_rows) return;
   const int w16 = (int)(row_bytes >> 4);
-  const u32x4* s = reinterpret_cast<const u32x4*>(src + r * row_bytes);
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + r * row_stride);
   u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)j * row_bytes);
   u32x4 v[4];
 #pragma unroll
@@ -121,15 +122,15 @@ int32_t hsp_device_read(const void* src, size_t bytes, int32_t blocks, uint32_t*
   return hsp_host_read(src, bytes, blocks, sink, stream);
 }
 
-int32_t hsp_host_gather(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
-                        int32_t n_rows, void* dst, hipStream_t stream) {
+int32_t hsp_host_gather(const void* src, int64_t src_rows, int64_t row_bytes, int64_t row_stride,
+                        const int64_t* rows, int32_t n_rows, void* dst, hipStream_t stream) {
   if (!src || !rows || !dst || n_rows < 0 || src_rows < 1 || row_bytes < 16 || row_bytes > 4096 ||
-      (row_bytes & 15))
+      (row_bytes & 15) || row_stride < row_bytes || (row_stride & 15))
     return (int32_t)hipErrorInvalidValue;
   if (n_rows == 0) return 0;
   const int blocks = (n_rows + kThreads / 64 - 1) / (kThreads / 64);
-  k_gather<<<blocks, kThreads, 0, stream>>>(static_cast<const uint8_t*>(src), src_rows, row_bytes, rows, n_rows,
-                                            static_cast<uint8_t*>(dst));
+  k_gather<<<blocks, kThreads, 0, stream>>>(static_cast<const uint8_t*>(src), src_rows, row_bytes, row_stride, rows,
+                                            n_rows, static_cast<uint8_t*>(dst));
   return (int32_t)hipGetLastError();
 }
 

@@ -535,9 +535,9 @@ template <int ROW_BYTES, bool FP8, bool FUSED>
 __device__ __forceinline__ void copy_part(const RsArgs& a, const StateView& v, const RsScratch& sc,
                                           int i, int c, uint32_t epoch) {
   constexpr int CH = ROW_BYTES / 16;        // 16-byte chunks of a pool row
-  constexpr int HCH = FP8 ? CH + 1 : CH;    // ... of a host row (fp8: then the chunk holding the scale)
-  constexpr int HSTRIDE = 16 * HCH;         // host row stride
-  static_assert(!FP8 || HSTRIDE == kHostRowStrideFp8, "fp8 host rows carry their scale");
+  constexpr int HCH = FP8 ? CH + 1 : CH;    // ... read of a host row (fp8: then the chunk holding the scale)
+  constexpr int HSTRIDE = FP8 ? kHostRowStrideFp8 : ROW_BYTES;  // host row stride
+  static_assert(16 * HCH <= HSTRIDE && HSTRIDE % 128 == 0, "host rows hold their chunks, 128-byte aligned");
   constexpr int CPL = (HCH + 63) / 64;      // chunks per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = v.top_k, lps = v.log2_ps;

@@ -6,9 +6,11 @@ Measures on the GPU at hand, with HIP events on the stream the probe
 kernels run on:
   * PCIe host read: zero-copy coalesced reads of a 512 MiB pinned, mapped
     host buffer (the kind of memory the pool's host store is), best of a
-    few grid sizes; and whole-row reads of random 1,152-byte (bf16) and
-    592-byte rows (576 fp8 code bytes and the row scale, padded to 16-byte
-    chunks, as the host store holds them), the miss copy's pattern;
+    few grid sizes; and reads of random rows as the miss copy makes them:
+    1,152-byte bf16 rows, and the 592 bytes of an fp8 row (576 code bytes
+    and the row scale, in 16-byte chunks) at the fp8 host row stride of 640
+    bytes (rows on 128-byte boundaries) and, for comparison, packed at a
+    592-byte stride;
   * HBM: a plain device copy (bytes read + written) and a plain device read;
   * MFMA: independent chains of the bf16 16x16x32 MFMA the attention kernel
     uses, counted at 16,384 FLOP each.
@@ -32,7 +34,7 @@ _SIGS = {
     "hsp_alloc_pinned": [_SZ, ctypes.POINTER(_VP)],
     "hsp_free_pinned": [_VP],
     "hsp_host_read": [_VP, _SZ, _I32, _VP, _VP],
-    "hsp_host_gather": [_VP, _I64, _I64, _VP, _I32, _VP, _VP],
+    "hsp_host_gather": [_VP, _I64, _I64, _I64, _VP, _I32, _VP, _VP],
     "hsp_device_copy": [_VP, _VP, _SZ, _I32, _VP],
     "hsp_device_read": [_VP, _SZ, _I32, _VP, _VP],
     "hsp_mfma_bf16": [_I32, _I32, _I32, _I32, _VP, _VP],
@@ -103,14 +105,14 @@ def measure(host_mib: int = 512, copy_mib: int = 1024, reps: int = 5) -> dict:
         out["pcie_host_read"] = {"bytes": nbytes, "gbs_by_grid": grids, "kind": "zero-copy coalesced 16-B loads"}
         rng = np.random.default_rng(1)
         gathers = {}
-        for rb in (1152, 592):
-            n_src = nbytes // rb
+        for rb, stride, key in ((1152, 1152, "1152"), (592, 640, "592"), (592, 592, "592_packed")):
+            n_src = nbytes // stride
             n = 65536
             rows = torch.from_numpy(rng.integers(0, n_src, size=n).astype(np.int64)).cuda()
             dst = torch.empty(n * rb, dtype=torch.uint8, device="cuda")
-            t = timed(lambda: _ok(L.hsp_host_gather(hp, n_src, rb, rows.data_ptr(), n, dst.data_ptr(), sp),
+            t = timed(lambda: _ok(L.hsp_host_gather(hp, n_src, rb, stride, rows.data_ptr(), n, dst.data_ptr(), sp),
                                   "hsp_host_gather"))
-            gathers[str(rb)] = round(n * rb / t / 1e9, 2)
+            gathers[key] = round(n * rb / t / 1e9, 2)
             del dst
         out["pcie_row_gather_gbs"] = gathers
     finally:

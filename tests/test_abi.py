@@ -39,8 +39,9 @@ def test_requirements_sizes():
     assert s.host_store_bytes == 16384 * 1152 and s.host_row_stride == 1152
     f8 = B.pool_requirements(desc(kv_dtype=B.HS_FP8_E4M3))
     assert f8.row_bytes == 576 and f8.pool_scale_bytes == 4 * 128 * 64
-    # an fp8 host row carries its scale: 576 code bytes + 4 + 12 unused
-    assert f8.host_row_stride == 592 and f8.host_store_bytes == 16384 * 592
+    # an fp8 host row carries its scale: 576 code bytes + 4 + 60 unused, so
+    # that rows start on 128-byte boundaries
+    assert f8.host_row_stride == 640 and f8.host_store_bytes == 16384 * 640
     assert B.pool_requirements(desc(kv_dtype=B.HS_F32)).row_bytes == 2304
 
 
