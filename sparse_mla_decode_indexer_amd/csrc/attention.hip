@@ -16,11 +16,11 @@
 //     or global_load_lds for pools over 4 GB; no registers), through a ring
 //     of three buffers: tiles t+1 and t+2 are in flight while tile t is
 //     computed, and the queries load under the first gathers; fp8 codes
-//     land raw and are widened to fp16 in LDS (exact);
-//     absent rows read zeros; rows sit 73 chunks of 16 bytes apart in
-//     LDS (one pad chunk), so the MFMA operand reads of 16 rows at one
-//     column hit distinct banks and operand addresses are a base plus an
-//     immediate offset;
+//     land raw and are widened to fp16 in registers after each operand
+//     read (exact); absent rows read zeros; rows sit 73 (bf16) or 37
+//     (fp8) chunks of 16 bytes apart in LDS (one pad chunk), so the MFMA
+//     operand reads of 16 rows at one column spread over the banks and
+//     operand addresses are a base plus an immediate offset;
 //   - wave (q block, half) computes the partial scores of its 16 queries over
 //     all 32 rows of the tile and its half (288) of the key dims,
 //     S^T (32 x 16 q) += K (32 x 288) . Q^T, with 16x16x32 bf16 MFMAs (its
@@ -37,9 +37,9 @@
 //     back exactly), so p enters as a single fp16 term (11 significant
 //     bits, round to nearest even) of p * row scale / the split's largest
 //     row scale: 16 PV MFMAs per tile instead of 32;
-//   - PV: O^T (256 dims x 16 q) += V^T . P^T; V^T operands come from 8x8
-//     register transposes of row-major LDS reads, in the same row order as
-//     P^T;
+//   - PV: O^T (256 dims x 16 q) += V^T . P^T; V^T operands come from LDS
+//     transpose loads of the row-major tile (16-bit elements for bf16 rows;
+//     8-bit codes, then widened, for fp8), in the same row order as P^T;
 //   - two workgroup barriers per tile: tile landed / previous tile retired,
 //     and the partial-score exchange; the gather of tile t + 2 is issued one
 //     DMA at a time between the QK MFMAs of tile t;
@@ -74,8 +74,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kTile = 32;              // rows per tile
 constexpr int kChunks = 2 * kRowDim / 16;        // 72 chunks of 16 B per bf16 row
 constexpr int kRowChunks = kChunks + 1;          // LDS row stride: 73 chunks (one pad chunk)
-constexpr int kTilePos = kTile * kRowChunks;     // 2336 chunk positions per tile
-constexpr int kTileBytes = kTilePos * 16;        // 37376
 constexpr int kRawChunks = kRowDim / 16;         // 36 chunks per fp8 row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -109,6 +107,24 @@ __device__ inline u32x2_t tr_load(const uint8_t* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
+// LDS transpose load of 8 x 8 bits (ds_read_b64_tr_b8): within each group
+// of 16 lanes, output lane j receives byte j % 8 of the 8 bytes addressed by
+// lanes 2e + j / 8 of the group, as its byte e (e = 0..7).
+__device__ inline u32x2_t tr8_load(const uint8_t* p) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p)));
+}
+
+// 8 OCP e4m3 codes (bytes 0..7) -> 8 fp16 in order (exact: every e4m3 value
+// is an fp16 value; the hardware conversion with scale 1).
+__device__ inline u32x4_t fp8x8_to_f16(u32x2_t w) {
+  return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.f, true))};
+}
+
 __device__ inline f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -135,23 +151,6 @@ static_assert(vmcnt_imm(0) == 0xF70 && vmcnt_imm(5) == 0xF75 && vmcnt_imm(38) ==
 // (truncation; exact when the values are representable in bf16).
 __device__ inline uint32_t pack_hi(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-}
-
-// 4 OCP e4m3 codes -> 4 bf16 (exact): decode to fp32 in hardware, keep the
-// upper halves.
-__device__ inline void fp8x4_to_bf16(uint32_t w, uint32_t* o) {
-  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  o[0] = pack_hi(f01[0], f01[1]);
-  o[1] = pack_hi(f23[0], f23[1]);
-}
-
-// 4 OCP e4m3 codes -> 4 fp16 (exact: every e4m3 value is an fp16 value).
-__device__ inline void fp8x4_to_f16(uint32_t w, uint32_t* o) {
-  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  o[0] = pack_f16(f01[0], f01[1]);
-  o[1] = pack_f16(f23[0], f23[1]);
 }
 
 // Workgroup barrier for LDS exchanges that leaves the tile prefetch in
@@ -206,9 +205,6 @@ __device__ inline int plan_entry(const PlanRef& p, int i, int j, uint32_t* err) 
   return u >= 0 ? pl[u] : -1;
 }
 
-// LDS chunk position of 16-byte chunk c of tile row r.
-__device__ inline int swz(int r, int c) { return r * kRowChunks + c; }
-
 template <bool FP8, int QB, bool BUF>
 __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     const uint16_t* __restrict__ q, int QR, PlanRef plan,
@@ -220,13 +216,17 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // the compiler can tell the DMA into one from the reads of another and
   // does not wait for the prefetch before computing. Each holds a tile plus
   // the landing area of the padding DMAs (see issue below).
-  constexpr int kPos = FP8 ? kTile * kRawChunks : kTilePos;  // chunk positions of a tile
+  // LDS row stride in 16-byte chunks: bf16 rows 72 + 1 pad, raw fp8 rows
+  // 36 + 1 pad (the pad chunks read zeros), so that operand reads of 16
+  // rows at one column spread over the banks
+  constexpr int kRowChunksT = FP8 ? kRawChunks + 1 : kRowChunks;
+  constexpr int kRowBytesT = 16 * kRowChunksT;
+  constexpr int kPos = kTile * kRowChunksT;  // chunk positions of a tile
   constexpr int kIssue = (kPos + 128 * QB - 1) / (128 * QB);  // DMAs per thread and tile
   constexpr int kBufBytes = kIssue * 128 * QB * 16;
   __shared__ __attribute__((aligned(16))) uint8_t bufA[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t bufB[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t bufC[kBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wide[FP8 ? kTileBytes : 16];
   __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
   __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
   __shared__ f32x4_t sbuf[2][QB][2][64];  // partial scores [key half][q block][row block][lane]
@@ -300,7 +300,6 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // the split read the zero row. With a fixed count per tile the wait for a
   // tile is a constant vmcnt, and the compiler, which counts the same
   // instructions, sees that the tile is complete and adds no wait of its own.
-  constexpr int kRowChunksT = FP8 ? kRawChunks : kRowChunks;
   // tile-invariant per position: the tile row and the byte offset in the
   // row (-1: pad chunk or past the tile), from one division, then stepped
   int rowk[kIssue], coff[kIssue];
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 #pragma unroll
     for (int k = 0; k < kIssue; ++k) {
       rowk[k] = min(r, kTile - 1);
-      coff[k] = (r < kTile && (FP8 || c < kChunks)) ? c * 16 : -1;
+      coff[k] = (r < kTile && c < (FP8 ? kRawChunks : kChunks)) ? c * 16 : -1;
       c += kStepC;
       r += kStepR;
       if (c >= kRowChunksT) {
@@ -353,12 +352,18 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // lane 4i + c reads dims 4c .. 4c+3 of row krow(kg, i) (first load) or
   // krow(kg, 4 + i) (second), and lane ln of the group receives dim ln of
   // those four rows: the A operand of 16 dims over rows krow(kg, 0..7).
+  // Raw fp8 rows (8-bit transpose loads): source lane 2e + h of a group
+  // reads dims 16b + 8h .. +8 of row krow(kg, e), and lane ln of the group
+  // receives dim ln of the rows krow(kg, 0..7), as 8 codes widened in
+  // registers.
   const int tr_i = (lane & 15) >> 2, tr_c = lane & 3;
-  const int v_off0 = krow(kg, tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
-  const int v_off1 = krow(kg, 4 + tr_i) * kRowChunks * 16 + (256 * half + 4 * tr_c) * 2;
-  // K operand reads (QK): lane (kg, ln) reads chunk 36*half + 4*kk + kg of
-  // tile row 16*rb + ln
-  const int k_off = swz(ln, 36 * half + kg) * 16;
+  const int v_off0 = FP8 ? krow(kg, (lane & 15) >> 1) * kRowBytesT + 256 * half + 8 * (lane & 1)
+                         : krow(kg, tr_i) * kRowBytesT + (256 * half + 4 * tr_c) * 2;
+  const int v_off1 = krow(kg, 4 + tr_i) * kRowBytesT + (256 * half + 4 * tr_c) * 2;  // (bf16 only)
+  // K operand reads (QK): lane (kg, ln) reads key dims 288*half + 32*kk +
+  // 8*kg .. +8 of tile row 16*rb + ln (16 bytes of bf16, or 8 fp8 codes
+  // widened in registers)
+  const int k_off = ln * kRowBytesT + (FP8 ? 288 * half + 8 * kg : (288 * half + 8 * kg) * 2);
   float m_run = -INFINITY, lpart = 0.f;
 
   // One tile: wait for it, start the gather of tile t + 2 into `nxt` (the
@@ -368,21 +373,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   auto tile = [&](int t, const uint8_t* cur, uint8_t* nxt) {
     __builtin_amdgcn_s_waitcnt(kWaitOne);  // this wave's part of tile t has landed
     lds_sync();                            // all of tile t is in LDS; tile t-1 is done
-    const uint8_t* T = FP8 ? wide : cur;
-    if (FP8) {  // widen the raw codes of tile t into the bf16 tile
-      for (int x = tid; x < kTile * kRawChunks; x += kAttThreads) {
-        const int r = x / kRawChunks, c = x - r * kRawChunks;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cur + x * 16);
-        uint32_t w[8];
-        fp8x4_to_f16(v[0], w);
-        fp8x4_to_f16(v[1], w + 2);
-        fp8x4_to_f16(v[2], w + 4);
-        fp8x4_to_f16(v[3], w + 6);
-        *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4_t*>(wide + swz(r, 2 * c + 1) * 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-      }
-      lds_sync();
-    }
+    const uint8_t* T = cur;
     // The gather of tile t + 2 goes out between the QK MFMAs below (one
     // DMA per key step): the CU's texture path moves a tile in about as
     // long as the QK phase takes, and DMAs issued all at once, by every
@@ -396,7 +387,12 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) ka[kk][rb] = *reinterpret_cast<const u32x4_t*>(Tk + (16 * rb * kRowChunks + 4 * kk) * 16);
+      for (int rb = 0; rb < 2; ++rb) {
+        if constexpr (FP8)
+          ka[kk][rb] = fp8x8_to_f16(*reinterpret_cast<const u32x2_t*>(Tk + 16 * rb * kRowBytesT + 32 * kk));
+        else
+          ka[kk][rb] = *reinterpret_cast<const u32x4_t*>(Tk + 16 * rb * kRowBytesT + 64 * kk);
+      }
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
 #pragma unroll
@@ -473,9 +469,13 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     u32x4_t va[16];
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
-      const u32x2_t x = tr_load(T + v_off0 + 32 * b);
-      const u32x2_t y = tr_load(T + v_off1 + 32 * b);
-      va[b] = u32x4_t{x[0], x[1], y[0], y[1]};
+      if constexpr (FP8) {
+        va[b] = fp8x8_to_f16(tr8_load(T + v_off0 + 16 * b));
+      } else {
+        const u32x2_t x = tr_load(T + v_off0 + 32 * b);
+        const u32x2_t y = tr_load(T + v_off1 + 32 * b);
+        va[b] = u32x4_t{x[0], x[1], y[0], y[1]};
+      }
     }
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
@@ -488,12 +488,13 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     }
     // Instruction order: the operand loads run kPvAhead blocks ahead of
     // their MFMAs, so LDS latency overlaps the MFMAs of earlier blocks.
-    constexpr int kPvMfma = FP8 ? 1 : 2;  // MFMAs per value block
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+    constexpr int kPvMfma = FP8 ? 1 : 2;   // MFMAs per value block
+    constexpr int kPvLoads = FP8 ? 1 : 2;  // transpose loads per value block
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPvLoads * kPvAhead, 0);
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvMfma, 0);
-      if (b + kPvAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      if (b + kPvAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPvLoads, 0);
     }
   };
 
@@ -564,8 +565,9 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   // 4 rows. Streaming stores: the rows are read once, by the merge kernel
   // or the caller.
   constexpr int kStgRow = 272;  // a query's 64 dims (256 bytes) + 16 (LDS banks)
-  static_assert(2 * QB * 16 * kStgRow <= (FP8 ? kTileBytes : kBufBytes), "staging fits the tile buffer");
-  uint8_t* stg = (FP8 ? wide : bufA) + wave * 16 * kStgRow;
+  constexpr int kStgPerBuf = kBufBytes / (16 * kStgRow);  // waves whose staging fits one ring buffer
+  static_assert(2 * kStgPerBuf >= 2 * QB, "staging fits two ring buffers");
+  uint8_t* stg = (wave < kStgPerBuf ? bufA + wave * 16 * kStgRow : bufB + (wave - kStgPerBuf) * 16 * kStgRow);
   const size_t row0 = n_splits == 1 ? (size_t)i * QR : ((size_t)i * n_splits + sp) * QR;
   float* const dst = n_splits == 1 ? out : part_o;
 #pragma unroll
