@@ -227,7 +227,12 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
   __shared__ __attribute__((aligned(16))) uint8_t bufB[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t bufC[kBufBytes];
   __shared__ int prow_s[kAttMaxTilesPerSplit * kTile];
-  __shared__ float scale_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
+  // Per-row softmax factors of the split: a row's base-2 logit is
+  // raw * f[0] + f[1] (f[1] = -inf for an absent row) and its weight
+  // p * f[2]; fp8: f = {c2 * scale, 0 or -inf, scale / sref}; bf16 rows
+  // keep only the absent-row term (f[0] = c2, f[2] = 1).
+  __shared__ f32x4_t rowf_s[FP8 ? kAttMaxTilesPerSplit * kTile : 1];
+  __shared__ float rmask_s[FP8 ? 1 : kAttMaxTilesPerSplit * kTile];
   __shared__ f32x4_t sbuf[2][QB][2][64];  // partial scores [key half][q block][row block][lane]
   __shared__ float smax_s[2 * QB];        // fp8: largest row scale seen by each wave
   constexpr int kAttThreads = 128 * QB;
@@ -258,11 +263,11 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       pr = -1;
     }
     prow_s[j] = pr;
-    if (FP8) scale_s[j] = pr >= 0 ? pool_scales[pr] : 0.f;
+    if (FP8) rowf_s[j][0] = pr >= 0 ? pool_scales[pr] : 0.f;  // (the scale, until sref is known)
   }
   if constexpr (FP8) {  // the split's largest row scale (the fp16 weights are relative to it)
     float mx = 0.f;
-    for (int j = tid; j < nt * kTile; j += kAttThreads) mx = fmaxf(mx, scale_s[j]);
+    for (int j = tid; j < nt * kTile; j += kAttThreads) mx = fmaxf(mx, rowf_s[j][0]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     if (lane == 0) smax_s[wave] = mx;
@@ -287,6 +292,17 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     if (mx > 0.f) {
       sref = mx;
       inv_sref = 1.f / mx;
+    }
+  }
+  // the rows' softmax factors (each thread its own entries; the first tile's
+  // barrier publishes them)
+  for (int j = tid; j < nt * kTile; j += kAttThreads) {
+    const bool present = prow_s[j] >= 0;
+    if constexpr (FP8) {
+      const float sc = rowf_s[j][0];
+      rowf_s[j] = f32x4_t{present ? c2 * sc : 0.f, present ? 0.f : -INFINITY, sc * inv_sref, 0.f};
+    } else {
+      rmask_s[j] = present ? 0.f : -INFINITY;
     }
   }
   int q_shift = 0;  // fp8: this wave's query half was scaled by 2^q_shift
@@ -418,14 +434,19 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
     sacc[0] += sbuf[half ^ 1][qb][0][lane];
     sacc[1] += sbuf[half ^ 1][qb][1][lane];
     // base-2 logits; lane holds rows krow(kg, e) of query ln
-    float s[8], rs[8];
+    float s[8], ws[8];
     float pm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = t * kTile + krow(kg, e);
-      rs[e] = FP8 ? scale_s[row] : 1.f;
       const float raw = e < 4 ? sacc[0][e] : sacc[1][e - 4];
-      s[e] = prow_s[row] >= 0 ? raw * (c2 * rs[e]) : -INFINITY;
+      if constexpr (FP8) {
+        const f32x4_t f = rowf_s[row];
+        s[e] = fmaf(raw, f[0], f[1]);
+        ws[e] = f[2];
+      } else {
+        s[e] = fmaf(raw, c2, rmask_s[row]);
+      }
       pm = fmaxf(pm, s[e]);
     }
     pm = max_across_kg(pm);
@@ -445,7 +466,7 @@ __global__ __launch_bounds__(128 * QB) void k_attn_mfma(
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(s[e] - m_use);
         psum += pe;
-        a[e] = FP8 ? pe * (rs[e] * inv_sref) : pe;
+        a[e] = FP8 ? pe * ws[e] : pe;
         lo[e] = a[e] - __uint_as_float(__float_as_uint(a[e]) & 0xFFFF0000u);
       }
       lpart = lpart * alpha + psum;
