@@ -85,6 +85,30 @@ def test_manager_under_budget_with_growth_fp8():
         rn.close()
 
 
+@pytest.mark.parametrize("ps,kv,budget", [(4, "fp8", 300), (1024, "bf16", 3)], ids=["page-4-fp8", "page-1024-bf16"])
+def test_manager_at_page_size_edges(ps, kv, budget):
+    """The manager with pages of 4 tokens (fp8 rows: each copied row carries
+    its scale into the host store) and of 1,024 tokens (bf16): every page
+    resident at the start without a host copy, a budget below the request's
+    pages, so each call copies pages to the host, then releases the coldest
+    ones, and later steps miss on them."""
+    spec = small("single-128k", ctx=8192, host_pages=0, page_size=ps, kv_dtype=kv, top_k=256,
+                 hot_rows=max(512, ps), scores=("ar1_shift", 0.9, 0.5))
+    wl = W.generate(spec)
+    rn = Runner(wl)
+    try:
+        _poison_gpu_pages_on_host(rn)
+        moved = np.zeros(2, dtype=np.int64)
+        for n in range(6):
+            rn.step(heads=[0, 77])
+            moved += _update_and_check(rn, [budget], 256, 128, f"page {ps} step {n + 1}")
+        log(f"[gpu] residency page {ps} {kv}: copied/demoted {moved.tolist()}")
+        assert moved[0] > 0 and moved[1] > 0
+        rn.step(heads=[0, 77])
+    finally:
+        rn.close()
+
+
 def test_manager_shrinking_budget_single_request():
     """One 128k-style request, all pages resident with valid host copies;
     the budget drops in large steps, so one call releases many pages at once
