@@ -150,17 +150,20 @@ def test_union_step_graph_replays_match_eager():
     _graph_vs_eager(_union_spec(steps=4), lambda pool, buf: Hn.decode_step(pool, buf, 0))
 
 
-@pytest.mark.parametrize("case", ["fp8-q1", "fp8-q4"])
-def test_fp8_step_graph_replays_match_eager(case):
+@pytest.mark.parametrize("case", ["fp8-q1", "fp8-q4", "f32"])
+def test_fp8_and_f32_step_graph_replays_match_eager(case):
     """A plain step over fp8 rows (one query token, and four sharing one
-    plan) captured in a hipGraph and replayed with new inputs, bit-identical
-    to eager steps: the attention widens the codes in registers."""
-    log(f"[gpu] fp8 step ({case}): hipGraph replays vs eager")
+    plan; the attention widens the codes in registers) or fp32 rows (split
+    vector attention and its merge) captured in a hipGraph and replayed with
+    new inputs, bit-identical to eager steps."""
+    log(f"[gpu] step ({case}): hipGraph replays vs eager")
     from sparse_mla_decode_indexer_amd import harness as Hn
     if case == "fp8-q1":
         spec = small("single-1m-fp8", ctx=40000, host_pages=563, scores=("ar1_shift", 0.95, 0.5), steps=4)
-    else:
+    elif case == "fp8-q4":
         spec = small("agent16", n_req=3, growth=(5000, 300, 40, 2), gpu_token_budget=2048, steps=20)
+    else:
+        spec = W.SPECS["tiny"]
     _graph_vs_eager(spec, lambda pool, buf: Hn.decode_step(pool, buf, 0))
 
 
