@@ -44,7 +44,7 @@ __device__ inline ix_f32x4_t ix_mfma(ix_u32x4_t a, ix_u32x4_t b, ix_f32x4_t c) {
 
 // HB = heads / 16. Grid (ceil(max_context / (256 * passes)), n_req).
 template <int HB>
-__global__ __launch_bounds__(kIxThreads) void k_indexer_scores(const uint16_t* __restrict__ iq,
+__global__ __launch_bounds__(kIxThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_indexer_scores(const uint16_t* __restrict__ iq,
                                                               const float* __restrict__ iw,
                                                               const uint16_t* __restrict__ ik,
                                                               int64_t ik_stride, const int32_t* __restrict__ req_ids,
@@ -74,23 +74,14 @@ __global__ __launch_bounds__(kIxThreads) void k_indexer_scores(const uint16_t* _
   float wv[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) wv[hb] = iw[(size_t)i * 16 * HB + 16 * hb + ln];
-  __syncthreads();
-  ix_u32x4_t qop[HB][4];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qop[hb][kk] = q_s[((16 * hb + ln) * kIxDim + 32 * kk + 8 * kg) / 8];
-  }
   const uint16_t* kr = ik + (size_t)rq * ik_stride * kIxDim;
   float* out = scores + (size_t)i * score_stride;
-
-  for (int p = 0; p < passes; ++p) {
-    const int t0 = t_wg + p * kIxPassTokens + wave * (kIxGroups * 16);
-    if (t0 >= L) break;
-    // A operands: lane (kg, ln) holds token t0 + 16g + ln (clamped into the
-    // context: tokens past it are computed on the last token and not
-    // written), dims 32kk + 8kg .. +8
-    ix_u32x4_t ka[kIxGroups][4];
+  // A operands: lane (kg, ln) holds token t0 + 16g + ln (clamped into the
+  // context: tokens past it are computed on the last token and not
+  // written), dims 32kk + 8kg .. +8. The first pass's keys are requested
+  // before the barrier, so that they load together with the queries.
+  ix_u32x4_t ka[kIxGroups][4];
+  auto load_keys = [&](int t0) {
 #pragma unroll
     for (int g = 0; g < kIxGroups; ++g) {
       const int t = min(t0 + 16 * g + ln, L - 1);
@@ -98,6 +89,20 @@ __global__ __launch_bounds__(kIxThreads) void k_indexer_scores(const uint16_t* _
       for (int kk = 0; kk < 4; ++kk)
         ka[g][kk] = *reinterpret_cast<const ix_u32x4_t*>(kr + (size_t)t * kIxDim + 32 * kk + 8 * kg);
     }
+  };
+  load_keys(t_wg + wave * (kIxGroups * 16));
+  __syncthreads();
+  ix_u32x4_t qop[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qop[hb][kk] = q_s[((16 * hb + ln) * kIxDim + 32 * kk + 8 * kg) / 8];
+  }
+
+  for (int p = 0; p < passes; ++p) {
+    const int t0 = t_wg + p * kIxPassTokens + wave * (kIxGroups * 16);
+    if (t0 >= L) break;
+    if (p > 0) load_keys(t0);
 #pragma unroll
     for (int g = 0; g < kIxGroups; ++g) {
       // D[token][head]: lane (kg, ln) holds head 16hb + ln of tokens
